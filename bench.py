@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark of the ctconv hot path on one MI355X.
+
+Default workload: the vocoder-style upsampler stack, bf16 storage with fp32
+accumulation, N = 8: ConvTranspose1d 512->256 (k16 s8 p4) on L_in = 2000,
+ELU, 256->128 (k10 s5 p3), ELU, 128->64 (k8 s4 p2).  Inputs are seeded
+synthetic data with the workload's shapes and distributions; the weights are
+prepacked once, outside the timed region.  One step = the three transposed
+convolutions and the two ELUs, every one a libctconv kernel.
+
+Metric: ConvTranspose TFLOP/s with F = 2*N*C_in*C_out*prod(k)*prod(L_in) per
+layer, summed over the stack, divided by the wall time of the timed steps.
+
+Prints one JSON line (rank 0).  --workload picks another workload (istft,
+upsampler2d, gather2d, gather2d_dil2, upsampler1d_small) for profiling.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ConvTranspose TFLOP/s (2*N*Cin*Cout*K*Lin) and % of MFMA/HBM roofline, 1 GPU"
+PEAK_MFMA = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # dense TFLOP/s
+PEAK_HBM = 8000.0  # GB/s
+ESIZE = {"f32": 4, "bf16": 2, "f16": 2}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="vocoder_stack")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-frames", type=int, default=150,
+                    help="input frames of one batch item for the oracle's timed sample")
+    return ap.parse_args()
+
+
+def layer_geometry(wl):
+    """Per layer: (layer, input spatial, output spatial, flops, algorithmic bytes)."""
+    from vision_upsampler_decoders_amd import ctconv as C
+
+    out = []
+    sp = tuple(wl.in_spatial)
+    es = ESIZE[wl.dtype]
+    for L in wl.layers:
+        osp = C.ctconv_output_shape(sp, L.kernel, L.stride, L.padding, L.output_padding,
+                                    L.dilation)
+        K = int(np.prod(L.kernel))
+        flops = 2 * wl.N * L.C_in * L.C_out * K * int(np.prod(sp))
+        nbytes = es * (wl.N * L.C_in * int(np.prod(sp)) + L.C_in * L.C_out * K
+                       + (L.C_out if L.bias else 0) + wl.N * L.C_out * int(np.prod(osp)))
+        out.append((L, sp, osp, flops, nbytes))
+        sp = osp
+    return out
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "vision_upsampler_decoders_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload):
+    """HBM traffic measured with rocprofv3 --pmc for this kernel source, if any."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+        ent = rec.get(workload)
+        if ent and ent.get("kernel_digest") == kernel_source_digest():
+            return ent.get("bytes_per_launch")
+    except (OSError, ValueError):
+        return None
+    return None
+
+
+def cpu_baseline(wl, frames):
+    """The oracle, as it stands, on one batch item and the first `frames` input
+    positions of the workload (every layer, and the ELUs of the stack)."""
+    import oracle
+    from synth import inputs as I
+
+    sp = tuple(wl.in_spatial)
+    if len(sp) == 1:
+        sub = (min(frames, sp[0]),)
+    else:  # 2-D: a band of rows
+        sub = (max(1, min(sp[0], frames // 8)), sp[1])
+    x = I.gen_x(wl, N=1, in_spatial=sub)
+    ws = [I.gen_w(wl, li) for li in range(len(wl.layers))]
+    bs = [I.gen_bias(wl, li) for li in range(len(wl.layers))]
+    flops = 0
+    t0 = time.perf_counter()
+    cur = x
+    for li, L in enumerate(wl.layers):
+        flops += 2 * L.C_in * L.C_out * int(np.prod(L.kernel)) * int(np.prod(cur.shape[2:]))
+        cur = oracle.conv_transpose(cur, ws[li], bs[li], L.stride, L.padding,
+                                    L.output_padding, L.dilation)
+        if wl.elu_between and li + 1 < len(wl.layers):
+            cur = oracle.elu(cur)
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"batch item 0, input {list(sub)} of {list(sp)}, all {len(wl.layers)} "
+                      f"layer(s){' with ELU between' if wl.elu_between else ''}; "
+                      f"{flops / 1e9:.2f} GFLOP in {dt:.2f} s, single-threaded float64",
+            "seconds": dt, "host_nproc": os.cpu_count()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    from synth import inputs as I
+    from vision_upsampler_decoders_amd import ctconv as C
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(3)
+    C.load()
+    torch.cuda.set_device(0)
+    wl = I.workload(args.workload)
+    geo = layer_geometry(wl)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[wl.dtype]
+
+    def dev(a):
+        if wl.dtype == "bf16":
+            return torch.from_numpy(I.bf16_bits(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a.astype(np.float32 if wl.dtype == "f32" else np.float16)).cuda()
+
+    log(f"workload {wl.name}: {wl.note}")
+    x = dev(I.gen_x(wl))
+    packed, biases, outs, elus = [], [], [], []
+    for li, (L, sp, osp, _, _) in enumerate(geo):
+        w = dev(I.gen_w(wl, li))
+        packed.append(C.prepack(w, L.stride))
+        b = I.gen_bias(wl, li)
+        biases.append(None if b is None else dev(b))
+        outs.append(torch.empty((wl.N, L.C_out) + osp, dtype=tdt, device="cuda"))
+        elus.append(torch.empty_like(outs[-1]) if (wl.elu_between and li + 1 < len(geo)) else None)
+        del w
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    n_layers = len(geo)
+
+    def step(ev=None):
+        cur = x
+        for li, (L, sp, osp, _, _) in enumerate(geo):
+            if ev is not None:
+                ev[li][0].record(stream)
+            C.forward(cur, packed[li], biases[li], L.C_out, L.kernel, L.stride, L.padding,
+                      L.output_padding, L.dilation, out=outs[li])
+            if ev is not None:
+                ev[li][1].record(stream)
+            cur = outs[li]
+            if elus[li] is not None:
+                if ev is not None:
+                    ev[n_layers + li][0].record(stream)
+                C.elu(cur, out=elus[li])
+                if ev is not None:
+                    ev[n_layers + li][1].record(stream)
+                cur = elus[li]
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: wall clock over exactly K steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # per-launch durations with HIP events on the launch stream (separate pass)
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in range(2 * n_layers)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    layer_ms = [float(np.mean([evs[k][li][0].elapsed_time(evs[k][li][1])
+                               for k in range(args.steps)])) for li in range(n_layers)]
+    elu_ms = [float(np.mean([evs[k][n_layers + li][0].elapsed_time(evs[k][n_layers + li][1])
+                             for k in range(args.steps)]))
+              for li in range(n_layers) if elus[li] is not None]
+
+    total_flops = sum(g[3] for g in geo)
+    ms_per_step = wall / args.steps * 1e3
+    value = total_flops / (wall / args.steps) / 1e12
+
+    layers = []
+    for li, (L, sp, osp, fl, nb) in enumerate(geo):
+        t = layer_ms[li] * 1e-3
+        route = C.ctconv_query_route(wl.N, L.C_in, L.C_out, sp, L.kernel, L.stride, L.padding,
+                                     L.output_padding, L.dilation,
+                                     {"f32": 0, "bf16": 1, "f16": 2}[wl.dtype])
+        t_mfma = fl / (PEAK_MFMA[wl.dtype] * 1e12)
+        t_hbm = nb / (PEAK_HBM * 1e9)
+        layers.append({
+            "layer": li, "C_in": L.C_in, "C_out": L.C_out, "kernel": list(L.kernel),
+            "stride": list(L.stride), "in": list(sp), "out": list(osp),
+            "route": {1: "polyphase", 2: "gather"}[route],
+            "us": round(layer_ms[li] * 1e3, 2),
+            "tflops": round(fl / t / 1e12, 2), "gbps": round(nb / t / 1e9, 1),
+            "bound": "mfma" if t_mfma >= t_hbm else "hbm",
+            "frac_roofline": round(max(t_mfma, t_hbm) / t, 4),
+            "frac_mfma": round(t_mfma / t, 4), "frac_hbm": round(t_hbm / t, 4),
+        })
+
+    # dominant kernel: the layer launch with the most time per step
+    dom = max(range(n_layers), key=lambda i: layer_ms[i])
+    Ld = layers[dom]
+    fl_d, nb_d = geo[dom][3], geo[dom][4]
+    t_d = layer_ms[dom] * 1e-3
+    if Ld["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": round(fl_d / t_d / 1e12, 2),
+                "peak": PEAK_MFMA[wl.dtype], "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(nb_d / t_d / 1e9, 1), "peak": PEAK_HBM,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = load_traffic(f"{wl.name}/layer{dom}")
+    roof["kernel"] = f"layer {dom} ({Ld['route']}), {Ld['C_in']}->{Ld['C_out']} k{Ld['kernel']} s{Ld['stride']}"
+    roof["algorithmic_per_launch"] = {"flop": fl_d, "bytes": nb_d}
+    roof["avg_launch_us"] = Ld["us"]
+
+    t_roof = sum(max(g[3] / (PEAK_MFMA[wl.dtype] * 1e12), g[4] / (PEAK_HBM * 1e9)) for g in geo)
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": wl.name, "description": wl.note, "N": wl.N,
+                   "in_spatial": list(wl.in_spatial), "parallelism": "none (1 GPU)",
+                   "layers": [{"C_in": g[0].C_in, "C_out": g[0].C_out, "k": list(g[0].kernel),
+                               "s": list(g[0].stride), "p": list(g[0].padding),
+                               "op": list(g[0].output_padding), "d": list(g[0].dilation)}
+                              for g in geo]},
+        "roofline": roof,
+        "step_roofline_fraction": round(t_roof / (ms_per_step * 1e-3), 4),
+        "layers": layers,
+        "elu_us": [round(v * 1e3, 2) for v in elu_ms],
+        "gflop_per_step": round(total_flops / 1e9, 3),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_frames)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

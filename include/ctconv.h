@@ -1,0 +1,167 @@
+/*
+ * ctconv.h -- dense transposed convolution (ConvTranspose1d/2d, groups = 1)
+ * on AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * Operation (scatter definition).  Every input element x[n, ci, i] adds
+ * x[n, ci, i] * w[ci, co, t] to the output element at o = i*s - p + t*d for
+ * each output channel co and tap t, when 0 <= o < L_out; the optional bias is
+ * added once to every output.  Per dimension
+ *     L_out = (L_in - 1)*s - 2*p + d*(k - 1) + op + 1.
+ * The weight layout [C_in, C_out, k...] (un-flipped) and the tap condition are
+ * those of the gather-form kernel "conv_transpose2d.wgsl" in ExecuTorch PR
+ * #20849 ("[ExecuTorch][WebGPU] Add optimized conv2d op", Implementation).
+ *
+ * Two routes compute it:
+ *  - polyphase: when every kernel size is a multiple of its stride (k = m*s),
+ *    dilation is 1 and output_padding is 0, the operation is one stride-1
+ *    m-tap convolution producing every output phase, followed by a phase
+ *    interleave (depth-to-space) and a padding slice -- ExecuTorch PR #25037
+ *    ("[XNNPACK] Lower dense transposed convs as one polyphase conv + depth to
+ *    space", Summary formula).  Here it runs as an implicit GEMM on the MFMA
+ *    matrix cores with the interleave, slice and bias fused into its epilogue.
+ *  - gather: every other shape, one output at a time from the tap condition.
+ *
+ * Layouts.  x [N, C_in, L] or [N, C_in, H, W]; y [N, C_out, L_out] or
+ * [N, C_out, H_out, W_out]; bias [C_out]; all dense row-major (contiguous).
+ * One element type covers x, w, bias and y; products are accumulated in fp32
+ * and rounded once (round to nearest even) to the output type.
+ *
+ * Ownership.  The caller allocates and owns every buffer.  The library never
+ * allocates, frees, retains or aliases caller memory, and holds no global
+ * mutable state; all functions are thread-safe.
+ *
+ * Streams.  Device work is enqueued on `stream` (a hipStream_t; NULL is the
+ * default stream) and the call returns without synchronising.  Errors found
+ * on the host are returned before anything is enqueued, so outputs are left
+ * untouched; CTCONV_ERR_HIP reports a failed launch (hipGetLastError).
+ */
+#ifndef CTCONV_H
+#define CTCONV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CTCONV_ABI_VERSION 1
+
+typedef enum {
+    CTCONV_F32 = 0,  /* float32 storage, fp32 products */
+    CTCONV_BF16 = 1, /* bfloat16 storage, fp32 accumulation */
+    CTCONV_F16 = 2   /* float16 storage, fp32 accumulation */
+} ctconv_dtype;
+
+typedef enum {
+    CTCONV_OK = 0,
+    CTCONV_ERR_NULL = 1,  /* a required pointer is NULL */
+    CTCONV_ERR_SHAPE = 2, /* sizes out of range, or an output size below 1 */
+    CTCONV_ERR_PARAM = 3, /* ndim, stride, padding, dilation, output_padding or route invalid */
+    CTCONV_ERR_DTYPE = 4, /* unknown dtype */
+    CTCONV_ERR_ALIGN = 5, /* a device pointer is not 16-byte aligned */
+    CTCONV_ERR_HIP = 6    /* the HIP runtime reported an error while enqueuing */
+} ctconv_status;
+
+typedef enum {
+    CTCONV_ROUTE_AUTO = 0,      /* polyphase when eligible, else gather */
+    CTCONV_ROUTE_POLYPHASE = 1, /* force the MFMA polyphase kernel (ERR_PARAM if ineligible) */
+    CTCONV_ROUTE_GATHER = 2     /* force the gather kernel (valid for every shape) */
+} ctconv_route;
+
+/* Version of this ABI (CTCONV_ABI_VERSION). */
+int ctconv_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* ctconv_status_string(ctconv_status status);
+
+/*
+ * Output spatial size (host only, no device call).
+ *   ndim            1 or 2
+ *   in_spatial[d]   >= 0      kernel[d], stride[d], dilation[d] >= 1
+ *   padding[d]      >= 0      0 <= output_padding[d] < max(stride[d], dilation[d])
+ *   out_spatial[d]  receives (in-1)*s - 2p + d*(k-1) + op + 1, which must be >= 1
+ * Returns CTCONV_ERR_NULL / _PARAM / _SHAPE on invalid input, writing nothing.
+ */
+ctconv_status ctconv_output_shape(int ndim, const int64_t* in_spatial, const int64_t* kernel,
+                                  const int64_t* stride, const int64_t* padding,
+                                  const int64_t* output_padding, const int64_t* dilation,
+                                  int64_t* out_spatial);
+
+/*
+ * Size in bytes of the packed weight that ctconv_prepack writes (host only).
+ * The packed layout is phase-major: [P][C_out][T][C_in_pad] where
+ *   P = prod_d s_d output phases (phase (jy, jx) at jy*s_x + jx),
+ *   T = prod_d ceil(k_d / s_d) taps per phase (tap (ry, rx) at ry*m_x + rx),
+ *   C_in_pad = C_in rounded up to a multiple of 32,
+ * holding w[ci, co, s_y*ry + jy, s_x*rx + jx], and zero where a tap index
+ * reaches past the kernel or ci >= C_in.
+ */
+ctconv_status ctconv_packed_bytes(int ndim, int64_t C_in, int64_t C_out, const int64_t* kernel,
+                                  const int64_t* stride, ctconv_dtype dtype, size_t* bytes);
+
+/*
+ * Rearrange a ConvTranspose weight w [C_in, C_out, k...] (device memory) into
+ * the phase-major packed layout above (device memory of ctconv_packed_bytes
+ * bytes, caller-allocated).  An exact copy: no arithmetic.  Asynchronous on
+ * `stream`.  Both pointers must be 16-byte aligned.
+ */
+ctconv_status ctconv_prepack(const void* w, void* packed_w, int ndim, int64_t C_in, int64_t C_out,
+                             const int64_t* kernel, const int64_t* stride, ctconv_dtype dtype,
+                             void* stream);
+
+/*
+ * y = ConvTranspose(x, w, bias) on the device.
+ *   x          device, [N, C_in, in_spatial...]
+ *   packed_w   device, written by ctconv_prepack with the same C_in, C_out,
+ *              kernel, stride and dtype (a precondition the library cannot check)
+ *   bias       device [C_out], or NULL for none
+ *   y          device, [N, C_out, out_spatial...] (see ctconv_output_shape);
+ *              every element is written.  Must not overlap x, packed_w or bias.
+ *   N >= 0, C_in >= 1, C_out >= 1; other arguments as in ctconv_output_shape.
+ * Pointers must be 16-byte aligned.  With N = 0 nothing is enqueued.
+ */
+ctconv_status ctconv_forward(const void* x, const void* packed_w, const void* bias, void* y,
+                             int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                             const int64_t* in_spatial, const int64_t* kernel,
+                             const int64_t* stride, const int64_t* padding,
+                             const int64_t* output_padding, const int64_t* dilation,
+                             ctconv_dtype dtype, void* stream);
+
+/*
+ * ctconv_forward with an explicit route, so the two kernels can be checked
+ * against each other on shapes both support.  CTCONV_ROUTE_POLYPHASE on a
+ * shape outside the polyphase form returns CTCONV_ERR_PARAM.
+ */
+ctconv_status ctconv_forward_route(const void* x, const void* packed_w, const void* bias, void* y,
+                                   int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                                   const int64_t* in_spatial, const int64_t* kernel,
+                                   const int64_t* stride, const int64_t* padding,
+                                   const int64_t* output_padding, const int64_t* dilation,
+                                   ctconv_dtype dtype, ctconv_route route, void* stream);
+
+/*
+ * Which kernel ctconv_forward would run for these arguments (host only):
+ * writes CTCONV_ROUTE_POLYPHASE or CTCONV_ROUTE_GATHER to *route.
+ */
+ctconv_status ctconv_query_route(int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                                 const int64_t* in_spatial, const int64_t* kernel,
+                                 const int64_t* stride, const int64_t* padding,
+                                 const int64_t* output_padding, const int64_t* dilation,
+                                 ctconv_dtype dtype, ctconv_route* route);
+
+/*
+ * Exponential linear unit with alpha = 1, y = x > 0 ? x : exp(x) - 1,
+ * elementwise over n elements (device memory, computed in fp32, rounded once
+ * to dtype).  It is the activation between stacked upsampler layers, a case
+ * the test plan of ExecuTorch PR #25037 covers (transposed convs in sequence
+ * with an ELU between them).
+ * x and y may be the same buffer.
+ */
+ctconv_status ctconv_elu(const void* x, void* y, int64_t n, ctconv_dtype dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CTCONV_H */

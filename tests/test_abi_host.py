@@ -1,0 +1,170 @@
+"""Host-only checks of the C ABI (no device call is made by any of these).
+
+* the library loads and exports every function include/ctconv.h declares;
+* ctconv_output_shape agrees with the oracle's output length and rejects
+  invalid parameters;
+* ctconv_packed_bytes follows the documented packed layout size;
+* argument validation returns the documented status before any launch;
+* routing: shapes with k = m*s, dilation 1 and no output_padding take the
+  polyphase kernel, the rest the gather kernel.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from vision_upsampler_decoders_amd import ctconv as C
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(C.LIB_PATH):
+        from vision_upsampler_decoders_amd import build
+
+        build.build()
+    return C.load()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "ctconv.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ctconv_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(C.EXPORTED)
+    assert C.ctconv_abi_version() == 1
+    assert "aligned" in C.ctconv_status_string(5)
+
+
+@pytest.mark.parametrize("args", [
+    ((2000,), 16, 8, 4, 0, 1), ((16000,), 10, 5, 3, 0, 1), ((79999,), 8, 4, 2, 0, 1),
+    ((345,), 4096, 1024, 0, 0, 1), ((64, 64), 4, 2, 1, 0, 1), ((96, 96), 3, 2, 1, 1, 1),
+    ((96, 96), 3, 2, 1, 1, 2), ((7, 5), (3, 2), (2, 1), (1, 0), (1, 0), (1, 3)),
+    ((0,), 4096, 1024, 0, 0, 1), ((1,), 1, 1, 0, 0, 1), ((3,), 5, 2, 2, 3, 4),
+])
+def test_output_shape_matches_oracle(lib, oracle_mod, args):
+    sp, k, s, p, op, d = args
+    assert C.ctconv_output_shape(sp, k, s, p, op, d) == oracle_mod.output_shape(sp, k, s, p, op, d)
+
+
+@pytest.mark.parametrize("args,status", [
+    (((8,), 4, 2, 9, 0, 1), 2),    # output length below 1
+    (((8,), 0, 2, 0, 0, 1), 3),    # kernel 0
+    (((8,), 4, 0, 0, 0, 1), 3),    # stride 0
+    (((8,), 4, 2, -1, 0, 1), 3),   # negative padding
+    (((8,), 4, 2, 0, 2, 1), 3),    # output_padding >= max(stride, dilation)
+    (((8,), 4, 2, 0, 0, 0), 3),    # dilation 0
+    (((-1,), 4, 2, 0, 0, 1), 2),   # negative length
+    (((1 << 62,), 4, 8, 0, 0, 1), 2),  # overflow
+])
+def test_output_shape_rejects(lib, args, status):
+    with pytest.raises(C.CtconvError) as e:
+        C.ctconv_output_shape(*args)
+    assert e.value.status == status
+
+
+def test_output_shape_rejects_bad_ndim_and_null(lib):
+    a = (ctypes.c_int64 * 1)(4)
+    out = (ctypes.c_int64 * 1)()
+    assert lib.ctconv_output_shape(3, a, a, a, a, a, a, out) == 3
+    assert lib.ctconv_output_shape(1, None, a, a, a, a, a, out) == 1
+    assert lib.ctconv_output_shape(1, a, a, a, a, a, a, None) == 1
+
+
+@pytest.mark.parametrize("ndim,C_in,C_out,k,s,dt,expect", [
+    (1, 64, 32, (8,), (4,), 0, 4 * 32 * 2 * 64 * 4),
+    (1, 512, 256, (16,), (8,), 1, 8 * 256 * 2 * 512 * 2),
+    (1, 256, 128, (10,), (5,), 1, 5 * 128 * 2 * 256 * 2),
+    (1, 4098, 1, (4096,), (1024,), 0, 1024 * 1 * 4 * 4128 * 4),
+    (2, 256, 128, (4, 4), (2, 2), 1, 4 * 128 * 4 * 256 * 2),
+    (2, 128, 64, (3, 3), (2, 2), 0, 4 * 64 * 4 * 128 * 4),
+    (1, 3, 5, (7,), (3,), 2, 3 * 5 * 3 * 32 * 2),
+])
+def test_packed_bytes(lib, ndim, C_in, C_out, k, s, dt, expect):
+    assert C.ctconv_packed_bytes(ndim, C_in, C_out, k, s, dt) == expect
+
+
+def test_packed_bytes_rejects(lib):
+    for args, st in [((1, 0, 4, (4,), (2,), 0), 2), ((1, 4, 0, (4,), (2,), 0), 2),
+                     ((1, 4, 4, (0,), (2,), 0), 3), ((1, 4, 4, (4,), (2,), 7), 4)]:
+        with pytest.raises(C.CtconvError) as e:
+            C.ctconv_packed_bytes(*args)
+        assert e.value.status == st
+    a = (ctypes.c_int64 * 3)(4, 4, 4)
+    nb = ctypes.c_size_t(0)
+    assert lib.ctconv_packed_bytes(3, 4, 4, a, a, 0, ctypes.byref(nb)) == 3
+    assert lib.ctconv_packed_bytes(1, 4, 4, a, a, 0, None) == 1
+
+
+def _fwd(lib, x=0x1000, w=0x2000, b=None, y=0x3000, N=1, C_in=4, C_out=4, sp=(8,), k=4, s=2,
+         p=1, op=0, d=1, dt=0, route=0):
+    nd = len(sp)
+    arr = lambda v: (ctypes.c_int64 * nd)(*C.per_dim(v, nd))  # noqa: E731
+    return lib.ctconv_forward_route(x, w, b, y, N, C_in, C_out, nd, arr(sp), arr(k), arr(s),
+                                    arr(p), arr(op), arr(d), dt, route, None)
+
+
+def test_forward_validation_before_launch(lib):
+    # Every call below must be rejected on the host: none reaches a launch.
+    assert _fwd(lib, x=None) == 1
+    assert _fwd(lib, w=None) == 1
+    assert _fwd(lib, y=None) == 1
+    assert _fwd(lib, C_in=0) == 2
+    assert _fwd(lib, C_out=0) == 2
+    assert _fwd(lib, N=-1) == 2
+    assert _fwd(lib, dt=9) == 4
+    assert _fwd(lib, s=0) == 3
+    assert _fwd(lib, op=2) == 3
+    assert _fwd(lib, p=9) == 2
+    assert _fwd(lib, route=7) == 3
+    assert _fwd(lib, x=0x1001) == 5
+    assert _fwd(lib, y=0x3008) == 5
+    assert _fwd(lib, b=0x4004) == 5
+    # polyphase forced on a shape outside the polyphase form
+    assert _fwd(lib, k=3, route=1) == 3
+    assert _fwd(lib, op=1, route=1) == 3
+    assert _fwd(lib, d=2, k=4, route=1) == 3
+    assert lib.ctconv_elu(None, 0x1000, 4, 0, None) == 1
+    assert lib.ctconv_elu(0x1000, 0x2000, -1, 0, None) == 2
+    assert lib.ctconv_elu(0x1000, 0x2000, 4, 5, None) == 4
+    assert lib.ctconv_elu(0x1002, 0x2000, 4, 1, None) == 5
+
+
+def test_forward_with_N_zero_enqueues_nothing(lib):
+    assert _fwd(lib, N=0) == 0
+
+
+@pytest.mark.parametrize("name,route", [
+    ("upsampler1d_small", 1), ("vocoder_stack", 1), ("istft", 1), ("upsampler2d", 1),
+    ("gather2d", 2), ("gather2d_dil2", 2),
+])
+def test_routes_of_workloads(lib, name, route):
+    from synth import inputs as I
+
+    wl = I.workload(name)
+    dt = {"f32": 0, "bf16": 1, "f16": 2}[wl.dtype]
+    sp = wl.in_spatial
+    for L in wl.layers:
+        r = C.ctconv_query_route(wl.N, L.C_in, L.C_out, sp, L.kernel, L.stride, L.padding,
+                                 L.output_padding, L.dilation, dt)
+        assert r == route
+        sp = C.ctconv_output_shape(sp, L.kernel, L.stride, L.padding, L.output_padding,
+                                   L.dilation)
+
+
+@pytest.mark.parametrize("k,s,p,op,d,route", [
+    (8, 4, 2, 0, 1, 1), (6, 3, 0, 0, 1, 1), (4, 1, 1, 0, 1, 1), (3, 2, 1, 0, 1, 2),
+    (8, 4, 2, 1, 1, 2), (8, 4, 2, 0, 2, 2), (16, 4, 2, 0, 1, 1), (20, 4, 2, 0, 1, 2),
+])
+def test_route_rule(lib, k, s, p, op, d, route):
+    # polyphase iff k % s == 0, d == 1, op == 0 (and m = k/s within the compiled taps)
+    assert C.ctconv_query_route(2, 16, 16, (50,), k, s, p, op, d, 1) == route

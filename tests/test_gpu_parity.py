@@ -1,0 +1,420 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle on
+the same seeded inputs.
+
+Bars: relative L2 <= 1e-5 for fp32 and <= 1e-2 for bf16/fp16, against the
+float64 oracle evaluated on the storage-rounded inputs; bit-exact for the
+prepack copy and for impulse responses.
+"""
+
+import numpy as np
+import pytest
+
+from synth import inputs as I
+
+from gpu_util import TOL, sample_indices, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cc():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    from vision_upsampler_decoders_amd import ctconv
+
+    ctconv.load()
+    return ctconv
+
+
+def _run(cc, x64, w64, b64, dt, s, p, op=0, d=1, route=0, N=None):
+    import torch
+
+    x = to_dev(x64, dt)
+    w = to_dev(w64, dt)
+    b = None if b64 is None else to_dev(b64, dt)
+    k = tuple(w64.shape[2:])
+    pw = cc.prepack(w, s)
+    y = cc.forward(x, pw, b, w64.shape[1], k, s, p, op, d, route=route)
+    torch.cuda.synchronize()
+    return y
+
+
+def _rand(shape, seed, dt, lo=-1.0, hi=1.0):
+    return I.uniform(seed, shape, lo, hi, dt)
+
+
+# ---------------------------------------------------------------------------
+# prepack: bit-exact against the documented index map
+# ---------------------------------------------------------------------------
+
+
+def _pack_ref(w, s):
+    """packed[j][co][r][ci] = w[ci, co, sy*ry + jy, sx*rx + jx], zero padded."""
+    C_in, C_out = w.shape[:2]
+    k = w.shape[2:]
+    if len(k) == 1:
+        w = w[:, :, None, :]
+        k = (1,) + tuple(k)
+        s = (1, s[0])
+    kH, kW = k
+    sH, sW = s
+    mH, mW = -(-kH // sH), -(-kW // sW)
+    Cp = -(-C_in // 32) * 32
+    out = np.zeros((sH * sW, C_out, mH * mW, Cp), dtype=w.dtype)
+    for jy in range(sH):
+        for jx in range(sW):
+            for ry in range(mH):
+                for rx in range(mW):
+                    ty, tx = sH * ry + jy, sW * rx + jx
+                    if ty < kH and tx < kW:
+                        out[jy * sW + jx, :, ry * mW + rx, :C_in] = w[:, :, ty, tx].T
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("C_in,C_out,k,s,dt", [
+    (64, 32, (8,), (4,), "f32"), (37, 5, (7,), (3,), "bf16"), (16, 8, (3, 3), (2, 2), "f32"),
+    (40, 9, (4, 6), (2, 3), "f16"), (4098, 1, (4096,), (1024,), "f32"),
+])
+def test_prepack_bitwise(cc, C_in, C_out, k, s, dt):
+    say(f"prepack C_in={C_in} C_out={C_out} k={k} s={s} {dt}")
+    import torch
+
+    w64 = _rand((C_in, C_out) + k, 77, dt)
+    w = to_dev(w64, dt)
+    pw = cc.prepack(w, s)
+    torch.cuda.synchronize()
+    got = pw.cpu()
+    ref = _pack_ref(to_host(w), s)
+    assert got.numel() == ref.size
+    if dt == "f32":
+        np.testing.assert_array_equal(got.numpy().view(np.uint32),
+                                      ref.astype(np.float32).view(np.uint32))
+    else:
+        ref_t = torch.from_numpy(ref).to(got.dtype)
+        assert torch.equal(got.view(torch.int16), ref_t.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# full-tensor parity at sizes the oracle finishes in seconds
+# (several tiles in every GEMM dimension and a ragged tail)
+# ---------------------------------------------------------------------------
+
+FULL_CASES = [
+    # name, dt, N, C_in, C_out, spatial, k, s, p, op, d, bias
+    ("upsampler1d_small", "f32", 1, 64, 32, (256,), (8,), (4,), (2,), (0,), (1,), True),
+    ("voc_l1_short", "bf16", 2, 512, 256, (300,), (16,), (8,), (4,), (0,), (1,), False),
+    ("voc_l2_short", "bf16", 2, 256, 128, (700,), (10,), (5,), (3,), (0,), (1,), True),
+    ("voc_l3_short", "bf16", 2, 128, 64, (1500,), (8,), (4,), (2,), (0,), (1,), False),
+    ("istft_frames", "f32", 2, 4098, 1, (23,), (4096,), (1024,), (0,), (0,), (1,), False),
+    ("up2d_small", "bf16", 2, 256, 128, (20, 37), (4, 4), (2, 2), (1, 1), (0, 0), (1, 1), True),
+    ("gather2d_small", "f32", 1, 128, 64, (24, 29), (3, 3), (2, 2), (1, 1), (1, 1), (1, 1), False),
+    ("gather2d_dil2_small", "f32", 1, 128, 64, (24, 29), (3, 3), (2, 2), (1, 1), (1, 1), (2, 2),
+     True),
+    # ragged channel counts, m = 1, 3, 4, s = 1, odd lengths, fp16, asymmetric 2-D
+    ("ragged_c_m3", "f16", 3, 33, 17, (131,), (9,), (3,), (4,), (0,), (1,), True),
+    ("m1_k_eq_s", "bf16", 2, 48, 40, (257,), (4,), (4,), (0,), (0,), (1,), True),
+    ("m4_s2", "f32", 2, 70, 24, (150,), (8,), (2,), (3,), (0,), (1,), True),
+    ("s1_k3", "f32", 2, 20, 18, (200,), (3,), (1,), (1,), (0,), (1,), False),
+    ("narrow_cout3", "f32", 2, 64, 3, (300,), (12,), (6,), (0,), (0,), (1,), True),
+    ("narrow_cout1_pad", "bf16", 2, 64, 1, (300,), (12,), (6,), (2,), (0,), (1,), True),
+    ("s16_subset", "bf16", 1, 96, 32, (90,), (32,), (16,), (8,), (0,), (1,), True),
+    ("asym2d", "f32", 2, 36, 20, (17, 45), (2, 6), (1, 3), (0, 2), (0, 0), (1, 1), True),
+    ("asym2d_m1", "bf16", 1, 64, 48, (33, 18), (2, 4), (2, 2), (0, 1), (0, 0), (1, 1), False),
+    ("len1", "f32", 3, 40, 16, (1,), (8,), (4,), (2,), (0,), (1,), True),
+]
+
+
+_ORACLE_CACHE = {}
+
+
+@pytest.mark.parametrize("case", FULL_CASES, ids=[c[0] for c in FULL_CASES])
+@pytest.mark.parametrize("route", [0, 2], ids=["auto", "gather"])
+def test_full_parity(cc, case, route):
+    name, dt, N, C_in, C_out, sp, k, s, p, op, d, has_b = case
+    if route == 2 and C_in * C_out * int(np.prod(k)) * N * int(np.prod(sp)) > 4e9:
+        pytest.skip("gather cross-check limited to small cases")
+    say(f"full_parity {name} route={route} dt={dt} N={N} C_in={C_in} C_out={C_out} sp={sp}")
+    seed = 500 + len(name)
+    x64 = I.normal(seed, (N, C_in) + sp, 1.0, dt)
+    w64 = I.normal(seed + 1, (C_in, C_out) + k, (C_in * np.prod(k)) ** -0.5, dt)
+    b64 = _rand((C_out,), seed + 2, dt, -0.1, 0.1) if has_b else None
+    if name.startswith("istft"):
+        w64 = I.istft_basis(4096, dt)
+    y = to_host(_run(cc, x64, w64, b64, dt, s, p, op, d, route=route))
+    from oracle import conv_transpose, rel_l2
+
+    if name not in _ORACLE_CACHE:
+        _ORACLE_CACHE[name] = conv_transpose(x64, w64, b64, s, p, op, d)
+    ref = _ORACLE_CACHE[name]
+    assert y.shape == ref.shape
+    err = rel_l2(y, ref)
+    say(f"  rel_l2 = {err:.3e}")
+    assert err <= TOL[dt], err
+
+
+# ---------------------------------------------------------------------------
+# full workload sizes, in the launch configuration the benchmark times:
+# sampled outputs computed one by one by the oracle
+# ---------------------------------------------------------------------------
+
+
+def _check_points(y_dev, x64, w64, b64, dt, s, p, op, d, seed, n_random=1500, extra=()):
+    import torch
+
+    from oracle import conv_transpose_points, rel_l2
+
+    idx = sample_indices(tuple(y_dev.shape), n_random, seed, extra)
+    it = torch.from_numpy(idx).to(y_dev.device)
+    if y_dev.dim() == 3:
+        got = y_dev[it[:, 0], it[:, 1], it[:, 3]]
+    else:
+        got = y_dev[it[:, 0], it[:, 1], it[:, 2], it[:, 3]]
+    got = got.to(torch.float64).cpu().numpy()
+    ref = conv_transpose_points(x64, w64, b64, idx, s, p, op, d)
+    err = rel_l2(got, ref)
+    say(f"  sampled {len(idx)} outputs: rel_l2 = {err:.3e}")
+    assert err <= TOL[dt], err
+    return err
+
+
+def test_vocoder_stack_full_size_per_layer(cc):
+    """Each layer checked on sampled outputs with the oracle fed the GPU's own
+    bf16 layer input; the ELU between layers checked element by element."""
+    import torch
+
+    from oracle import elu as oelu
+    from oracle import rel_l2
+
+    wl = I.workload("vocoder_stack")
+    x64 = I.gen_x(wl)
+    x = to_dev(x64, wl.dtype)
+    for li, L in enumerate(wl.layers):
+        say(f"vocoder layer {li}: {tuple(x.shape)} -> C_out {L.C_out} k{L.kernel} s{L.stride}")
+        w64 = I.gen_w(wl, li)
+        pw = cc.prepack(to_dev(w64, wl.dtype), L.stride)
+        y = cc.forward(x, pw, None, L.C_out, L.kernel, L.stride, L.padding)
+        torch.cuda.synchronize()
+        xin64 = to_host(x)
+        s_out = L.stride[0]
+        edges = [t * s_out * 128 + e for t in range(1, 6) for e in (-1, 0, 1)]
+        _check_points(y, xin64, w64, None, wl.dtype, L.stride, L.padding, 0, 1, 900 + li,
+                      extra=edges)
+        if li + 1 < len(wl.layers):
+            ye = cc.elu(y)
+            torch.cuda.synchronize()
+            got = to_host(ye[:2])
+            ref = oelu(to_host(y[:2]))
+            err = rel_l2(got, ref)
+            say(f"  elu rel_l2 = {err:.3e}")
+            assert err <= 1e-2
+            x = ye
+
+
+def test_vocoder_stack_end_to_end_short(cc):
+    """L1 -> ELU -> L2 -> ELU -> L3 against the oracle chain in float64."""
+    import torch
+
+    from oracle import conv_transpose, elu as oelu, rel_l2
+
+    wl = I.workload("vocoder_stack")
+    x64 = I.gen_x(wl, N=1, in_spatial=(60,))
+    x = to_dev(x64, wl.dtype)
+    ref = x64
+    for li, L in enumerate(wl.layers):
+        w64 = I.gen_w(wl, li)
+        pw = cc.prepack(to_dev(w64, wl.dtype), L.stride)
+        x = cc.forward(x, pw, None, L.C_out, L.kernel, L.stride, L.padding)
+        ref = conv_transpose(ref, w64, None, L.stride, L.padding)
+        if li + 1 < len(wl.layers):
+            x = cc.elu(x)
+            ref = oelu(ref)
+    torch.cuda.synchronize()
+    err = rel_l2(to_host(x), ref)
+    say(f"vocoder end-to-end short: rel_l2 = {err:.3e}")
+    assert err <= 1e-2
+
+
+def test_istft_full_size(cc):
+    """Whole output against the independent radix-2 irfft + overlap-add oracle."""
+    import torch
+
+    from oracle import istft_ola, rel_l2
+
+    wl = I.workload("istft")
+    L = wl.layers[0]
+    x64 = I.gen_x(wl)
+    w64 = I.gen_w(wl)
+    say("istft full size [8, 4098, 345] -> [8, 1, 356352]")
+    y = _run(cc, x64, w64, None, "f32", L.stride, L.padding)
+    ref = istft_ola(x64, 4096, 1024)
+    err = rel_l2(to_host(y)[:, 0], ref)
+    say(f"  rel_l2 vs irfft+OLA = {err:.3e}")
+    # the fp32-rounded basis itself differs from the exact transform by ~1e-8
+    assert err <= 1e-5
+    _check_points(y, x64, w64, None, "f32", L.stride, L.padding, 0, 1, 31, n_random=400)
+    del y
+    torch.cuda.empty_cache()
+
+
+def test_istft_perfect_reconstruction(cc):
+    """Spectra of Hann-windowed frames at hop n/4 resynthesise 1.5 z in the interior."""
+    from oracle import rel_l2
+
+    n_fft, hop, T = 4096, 1024, 40
+    z = I.normal(3011, ((T - 1) * hop + n_fft,), 1.0, "f32")
+    h = I.hann_periodic(n_fft)
+    F = n_fft // 2 + 1
+    spec = np.zeros((1, 2 * F, T))
+    for l in range(T):
+        X = np.fft.rfft(h * z[l * hop:l * hop + n_fft])
+        spec[0, :F, l] = X.real
+        spec[0, F:, l] = X.imag
+    spec = I.round_to_dtype(spec, "f32")
+    y = to_host(_run(cc, spec, I.istft_basis(n_fft, "f32"), None, "f32", (hop,), (0,)))[0, 0]
+    lo, hi = 3 * hop, (T - 1) * hop + hop
+    err = rel_l2(y[lo:hi], 1.5 * z[lo:hi])
+    say(f"istft reconstruction rel_l2 = {err:.3e}")
+    assert err <= 1e-5
+
+
+@pytest.mark.parametrize("name", ["upsampler2d", "gather2d", "gather2d_dil2", "upsampler1d_small"])
+def test_workload_full_size_sampled(cc, name):
+    import torch
+
+    wl = I.workload(name)
+    L = wl.layers[0]
+    x64 = I.gen_x(wl)
+    w64 = I.gen_w(wl)
+    b64 = I.gen_bias(wl)
+    say(f"{name} full size {x64.shape} dt={wl.dtype}")
+    y = _run(cc, x64, w64, b64, wl.dtype, L.stride, L.padding, L.output_padding, L.dilation)
+    _check_points(y, x64, w64, b64, wl.dtype, L.stride, L.padding, L.output_padding,
+                  L.dilation, 41, extra=[63, 64, 65, 127, 128, 129])
+    if name == "gather2d_dil2":
+        # even rows and columns receive no tap: bias or zero exactly
+        yh = y[:, :, 0::2, :].float()
+        assert float(yh.abs().max()) == 0.0
+        yh = y[:, :, :, 0::2].float()
+        assert float(yh.abs().max()) == 0.0
+    del y
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
+# exact special cases and edge cases
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("name", ["vocoder_l1", "upsampler2d", "gather2d_dil2", "istft"])
+def test_impulse_response_exact(cc, name):
+    """x = e_(n0, ci0, pos0): y equals the weight taps bit for bit, zero elsewhere."""
+    import torch
+
+    if name == "vocoder_l1":
+        dt, N, C_in, C_out, sp, k, s, p, op, d = "bf16", 8, 512, 256, (2000,), (16,), (8,), (4,), (0,), (1,)
+    elif name == "upsampler2d":
+        dt, N, C_in, C_out, sp, k, s, p, op, d = "bf16", 8, 256, 128, (64, 64), (4, 4), (2, 2), (1, 1), (0, 0), (1, 1)
+    elif name == "gather2d_dil2":
+        dt, N, C_in, C_out, sp, k, s, p, op, d = "f32", 4, 128, 64, (96, 96), (3, 3), (2, 2), (1, 1), (1, 1), (2, 2)
+    else:
+        dt, N, C_in, C_out, sp, k, s, p, op, d = "f32", 8, 4098, 1, (345,), (4096,), (1024,), (0,), (0,), (1,)
+    w64 = _rand((C_in, C_out) + k, 13, dt)
+    w = to_dev(w64, dt)
+    pw = cc.prepack(w, s)
+    for (n0, ci0, pos) in [(0, 0, tuple(0 for _ in sp)), (N - 1, C_in - 1, tuple(v - 1 for v in sp)),
+                           (N // 2, C_in // 2, tuple(v // 2 for v in sp))]:
+        say(f"impulse {name} at n={n0} ci={ci0} pos={pos}")
+        x = torch.zeros((N, C_in) + sp, dtype=w.dtype, device="cuda")
+        x[(n0, ci0) + pos] = 1.0
+        y = cc.forward(x, pw, None, C_out, k, s, p, op, d)
+        torch.cuda.synchronize()
+        ref = torch.zeros_like(y)
+        taps = [range(kk) for kk in k]
+        import itertools
+
+        for t in itertools.product(*taps):
+            o = tuple(pos[i] * s[i] - p[i] + t[i] * d[i] for i in range(len(sp)))
+            if all(0 <= o[i] < y.shape[2 + i] for i in range(len(sp))):
+                ref[(n0, slice(None)) + o] = w[(ci0, slice(None)) + t]
+        assert torch.equal(y, ref)
+
+
+def test_empty_input_and_null_bias(cc):
+    import torch
+
+    say("empty input: L_in = 0 with a non-empty output")
+    w = to_dev(_rand((6, 5, 4096), 3, "f32"), "f32")
+    pw = cc.prepack(w, (1024,))
+    b = to_dev(_rand((5,), 4, "f32"), "f32")
+    x = torch.zeros((2, 6, 0), dtype=torch.float32, device="cuda")
+    y = cc.forward(x, pw, b, 5, (4096,), (1024,), (0,))
+    torch.cuda.synchronize()
+    assert y.shape == (2, 5, 3072)
+    assert torch.equal(y, b.view(1, 5, 1).expand_as(y))
+    y0 = cc.forward(x, pw, None, 5, (4096,), (1024,), (0,))
+    torch.cuda.synchronize()
+    assert float(y0.abs().max()) == 0.0
+    say("N = 0: nothing to do")
+    x = torch.zeros((0, 6, 10), dtype=torch.float32, device="cuda")
+    y = cc.forward(x, pw, b, 5, (4096,), (1024,), (0,))
+    assert y.shape[0] == 0
+
+
+def test_fp16_cancellation(cc):
+    """Partial products beyond the fp16 range that cancel: fp32 accumulation
+    must return the small exact result."""
+    import torch
+
+    say("fp16 cancelling taps")
+    C_in, C_out, L = 2, 16, 40
+    x = torch.ones((1, C_in, L), dtype=torch.float16, device="cuda")
+    w = torch.zeros((C_in, C_out, 4), dtype=torch.float16, device="cuda")
+    w[0, :, :] = 40000.0
+    w[1, :, :] = -40000.0
+    w[1, :, 1] = -39968.0  # 40000 - 39968 = 32
+    for route in (0, 2):
+        pw = cc.prepack(w, (2,))
+        y = cc.forward(x, pw, None, C_out, (4,), (2,), (1,), route=route)
+        torch.cuda.synchronize()
+        yf = y.float().cpu().numpy()
+        assert np.isfinite(yf).all()
+        ref = to_host(x)
+        from oracle import conv_transpose
+
+        r = conv_transpose(ref, to_host(w), None, 2, 1)
+        np.testing.assert_array_equal(yf, r)
+
+
+def test_routes_agree(cc):
+    """Polyphase and gather kernels on the same polyphase-eligible shapes."""
+    import torch
+
+    from oracle import rel_l2
+
+    for dt, sp, k, s, p in [("f32", (300,), (8,), (4,), (2,)), ("bf16", (40, 50), (4, 4), (2, 2), (1, 1))]:
+        say(f"route cross-check {dt} {sp}")
+        x64 = I.normal(21, (2, 96) + sp, 1.0, dt)
+        w64 = I.normal(22, (96, 48) + k, 0.05, dt)
+        a = to_host(_run(cc, x64, w64, None, dt, s, p, route=1))
+        b = to_host(_run(cc, x64, w64, None, dt, s, p, route=2))
+        assert rel_l2(a, b) <= TOL[dt]
+
+
+def test_non_default_stream_and_determinism(cc):
+    import torch
+
+    say("non-default stream, repeated runs")
+    x64 = I.normal(31, (2, 256, 500), 1.0, "bf16")
+    w64 = I.normal(32, (256, 128, 10), 0.02, "bf16")
+    x, w = to_dev(x64, "bf16"), to_dev(w64, "bf16")
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        pw = cc.prepack(w, (5,), stream=st)
+        y1 = cc.forward(x, pw, None, 128, (10,), (5,), (3,), stream=st)
+        y2 = cc.forward(x, pw, None, 128, (10,), (5,), (3,), stream=st)
+    st.synchronize()
+    assert torch.equal(y1, y2)
+    y3 = cc.forward(x, pw, None, 128, (10,), (5,), (3,))
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y3)

@@ -1,0 +1,259 @@
+// C ABI of libctconv: argument validation, shape arithmetic, routing and
+// launches.  No allocation, no synchronisation, no global mutable state.
+
+#include <string.h>
+
+#include "ctconv_internal.h"
+
+using namespace ctconv;
+
+namespace {
+
+constexpr int64_t kI64Max = INT64_MAX;
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
+
+size_t esize(ctconv_dtype dt) { return dt == CTCONV_F32 ? 4 : 2; }
+
+bool dtype_ok(int dt) { return dt == CTCONV_F32 || dt == CTCONV_BF16 || dt == CTCONV_F16; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Per-dimension validation and output length (L-1)*s - 2p + d*(k-1) + op + 1.
+ctconv_status out_len(int64_t L, int64_t k, int64_t s, int64_t p, int64_t op, int64_t d,
+                      int64_t* out) {
+    if (L < 0) return CTCONV_ERR_SHAPE;
+    if (k < 1 || s < 1 || d < 1 || p < 0 || op < 0) return CTCONV_ERR_PARAM;
+    if (op >= (s > d ? s : d)) return CTCONV_ERR_PARAM;
+    int64_t a, b;
+    if (!mul_ok(L > 0 ? L - 1 : 0, s, &a) || !mul_ok(d, k - 1, &b)) return CTCONV_ERR_SHAPE;
+    // L = 0 contributes -s
+    __int128 v = (__int128)(L > 0 ? a : -s) - 2 * (__int128)p + b + op + 1;
+    if (v < 1) return CTCONV_ERR_SHAPE;
+    if (v > kI64Max) return CTCONV_ERR_SHAPE;
+    *out = (int64_t)v;
+    return CTCONV_OK;
+}
+
+ctconv_status geometry(int ndim, const int64_t* in_sp, const int64_t* kernel,
+                       const int64_t* stride, const int64_t* padding,
+                       const int64_t* output_padding, const int64_t* dilation, Problem* p) {
+    if (ndim != 1 && ndim != 2) return CTCONV_ERR_PARAM;
+    if (!in_sp || !kernel || !stride || !padding || !output_padding || !dilation)
+        return CTCONV_ERR_NULL;
+    int64_t in2[2] = {1, 1}, k2[2] = {1, 1}, s2[2] = {1, 1}, p2[2] = {0, 0}, op2[2] = {0, 0},
+            d2[2] = {1, 1}, o2[2] = {1, 1};
+    for (int i = 0; i < ndim; ++i) {
+        const int j = 2 - ndim + i;
+        in2[j] = in_sp[i];
+        k2[j] = kernel[i];
+        s2[j] = stride[i];
+        p2[j] = padding[i];
+        op2[j] = output_padding[i];
+        d2[j] = dilation[i];
+    }
+    for (int j = 2 - ndim; j < 2; ++j) {
+        const ctconv_status st = out_len(in2[j], k2[j], s2[j], p2[j], op2[j], d2[j], &o2[j]);
+        if (st != CTCONV_OK) return st;
+    }
+    p->ndim = ndim;
+    p->H = in2[0];
+    p->W = in2[1];
+    p->Ho = o2[0];
+    p->Wo = o2[1];
+    p->kH = k2[0];
+    p->kW = k2[1];
+    p->sH = s2[0];
+    p->sW = s2[1];
+    p->pH = p2[0];
+    p->pW = p2[1];
+    p->opH = op2[0];
+    p->opW = op2[1];
+    p->dH = d2[0];
+    p->dW = d2[1];
+    p->mH = (p->kH + p->sH - 1) / p->sH;
+    p->mW = (p->kW + p->sW - 1) / p->sW;
+    return CTCONV_OK;
+}
+
+// Channel counts, packed-layout sizes and element counts (all must fit int64).
+ctconv_status channels(int64_t N, int64_t C_in, int64_t C_out, ctconv_dtype dt, Problem* p) {
+    if (!dtype_ok(dt)) return CTCONV_ERR_DTYPE;
+    if (N < 0 || C_in < 1 || C_out < 1) return CTCONV_ERR_SHAPE;
+    if (C_in > kI64Max - kCinAlign) return CTCONV_ERR_SHAPE;
+    p->N = N;
+    p->C_in = C_in;
+    p->C_out = C_out;
+    p->dtype = dt;
+    p->C_in_pad = (C_in + kCinAlign - 1) / kCinAlign * kCinAlign;
+    int64_t P, T, t;
+    if (!mul_ok(p->sH, p->sW, &P) || !mul_ok(p->mH, p->mW, &T)) return CTCONV_ERR_SHAPE;
+    p->P = P;
+    p->T = T;
+    // packed weight elements and bytes
+    if (!mul_ok(P, C_out, &t) || !mul_ok(t, T, &t) || !mul_ok(t, p->C_in_pad, &t) ||
+        !mul_ok(t, (int64_t)esize(dt), &t))
+        return CTCONV_ERR_SHAPE;
+    // x and y element counts
+    if (!mul_ok(N, C_in, &t) || !mul_ok(t, p->H, &t) || !mul_ok(t, p->W, &t) ||
+        !mul_ok(t, (int64_t)esize(dt), &t))
+        return CTCONV_ERR_SHAPE;
+    if (!mul_ok(N, C_out, &t) || !mul_ok(t, p->Ho, &t) || !mul_ok(t, p->Wo, &t) ||
+        !mul_ok(t, (int64_t)esize(dt), &t))
+        return CTCONV_ERR_SHAPE;
+    return CTCONV_OK;
+}
+
+ctconv_status to_status(hipError_t e) { return e == hipSuccess ? CTCONV_OK : CTCONV_ERR_HIP; }
+
+ctconv_status build_problem(int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                            const int64_t* in_spatial, const int64_t* kernel,
+                            const int64_t* stride, const int64_t* padding,
+                            const int64_t* output_padding, const int64_t* dilation,
+                            ctconv_dtype dtype, Problem* p) {
+    memset(p, 0, sizeof(*p));
+    ctconv_status st =
+        geometry(ndim, in_spatial, kernel, stride, padding, output_padding, dilation, p);
+    if (st != CTCONV_OK) return st;
+    return channels(N, C_in, C_out, dtype, p);
+}
+
+bool polyphase_eligible(const Problem& p) {
+    // k a multiple of s in every dimension, no dilation, no output_padding.
+    return p.kH % p.sH == 0 && p.kW % p.sW == 0 && p.dH == 1 && p.dW == 1 && p.opH == 0 &&
+           p.opW == 0;
+}
+
+ctconv_route choose_route(const Problem& p) {
+    if (polyphase_eligible(p) && polyphase_supported(p)) return CTCONV_ROUTE_POLYPHASE;
+    return CTCONV_ROUTE_GATHER;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ctconv_abi_version(void) { return CTCONV_ABI_VERSION; }
+
+const char* ctconv_status_string(ctconv_status status) {
+    switch (status) {
+        case CTCONV_OK: return "ok";
+        case CTCONV_ERR_NULL: return "a required pointer is NULL";
+        case CTCONV_ERR_SHAPE: return "invalid or overflowing size";
+        case CTCONV_ERR_PARAM: return "invalid ndim, stride, padding, dilation, output_padding or route";
+        case CTCONV_ERR_DTYPE: return "unknown dtype";
+        case CTCONV_ERR_ALIGN: return "device pointer not 16-byte aligned";
+        case CTCONV_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+ctconv_status ctconv_output_shape(int ndim, const int64_t* in_spatial, const int64_t* kernel,
+                                  const int64_t* stride, const int64_t* padding,
+                                  const int64_t* output_padding, const int64_t* dilation,
+                                  int64_t* out_spatial) {
+    if (!out_spatial) return CTCONV_ERR_NULL;
+    Problem p;
+    memset(&p, 0, sizeof(p));
+    const ctconv_status st =
+        geometry(ndim, in_spatial, kernel, stride, padding, output_padding, dilation, &p);
+    if (st != CTCONV_OK) return st;
+    if (ndim == 1) {
+        out_spatial[0] = p.Wo;
+    } else {
+        out_spatial[0] = p.Ho;
+        out_spatial[1] = p.Wo;
+    }
+    return CTCONV_OK;
+}
+
+ctconv_status ctconv_packed_bytes(int ndim, int64_t C_in, int64_t C_out, const int64_t* kernel,
+                                  const int64_t* stride, ctconv_dtype dtype, size_t* bytes) {
+    if (!kernel || !stride || !bytes) return CTCONV_ERR_NULL;
+    if (ndim != 1 && ndim != 2) return CTCONV_ERR_PARAM;
+    const int64_t zeros[2] = {0, 0}, ones[2] = {1, 1};
+    Problem p;
+    ctconv_status st = build_problem(0, C_in, C_out, ndim, ones, kernel, stride, zeros, zeros,
+                                     ones, dtype, &p);
+    if (st != CTCONV_OK) return st;
+    int64_t t = p.P * p.C_out;  // overflow already checked in channels()
+    t = t * p.T * p.C_in_pad * (int64_t)esize(dtype);
+    *bytes = (size_t)t;
+    return CTCONV_OK;
+}
+
+ctconv_status ctconv_prepack(const void* w, void* packed_w, int ndim, int64_t C_in, int64_t C_out,
+                             const int64_t* kernel, const int64_t* stride, ctconv_dtype dtype,
+                             void* stream) {
+    if (!w || !packed_w || !kernel || !stride) return CTCONV_ERR_NULL;
+    if (ndim != 1 && ndim != 2) return CTCONV_ERR_PARAM;
+    const int64_t zeros[2] = {0, 0}, ones[2] = {1, 1};
+    Problem p;
+    ctconv_status st = build_problem(0, C_in, C_out, ndim, ones, kernel, stride, zeros, zeros,
+                                     ones, dtype, &p);
+    if (st != CTCONV_OK) return st;
+    if (!aligned16(w) || !aligned16(packed_w)) return CTCONV_ERR_ALIGN;
+    return to_status(launch_prepack(p, w, packed_w, static_cast<hipStream_t>(stream)));
+}
+
+ctconv_status ctconv_query_route(int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                                 const int64_t* in_spatial, const int64_t* kernel,
+                                 const int64_t* stride, const int64_t* padding,
+                                 const int64_t* output_padding, const int64_t* dilation,
+                                 ctconv_dtype dtype, ctconv_route* route) {
+    if (!route) return CTCONV_ERR_NULL;
+    Problem p;
+    const ctconv_status st = build_problem(N, C_in, C_out, ndim, in_spatial, kernel, stride,
+                                           padding, output_padding, dilation, dtype, &p);
+    if (st != CTCONV_OK) return st;
+    *route = choose_route(p);
+    return CTCONV_OK;
+}
+
+ctconv_status ctconv_forward_route(const void* x, const void* packed_w, const void* bias, void* y,
+                                   int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                                   const int64_t* in_spatial, const int64_t* kernel,
+                                   const int64_t* stride, const int64_t* padding,
+                                   const int64_t* output_padding, const int64_t* dilation,
+                                   ctconv_dtype dtype, ctconv_route route, void* stream) {
+    if (!x || !packed_w || !y) return CTCONV_ERR_NULL;
+    if (route != CTCONV_ROUTE_AUTO && route != CTCONV_ROUTE_POLYPHASE &&
+        route != CTCONV_ROUTE_GATHER)
+        return CTCONV_ERR_PARAM;
+    Problem p;
+    const ctconv_status st = build_problem(N, C_in, C_out, ndim, in_spatial, kernel, stride,
+                                           padding, output_padding, dilation, dtype, &p);
+    if (st != CTCONV_OK) return st;
+    if (!aligned16(x) || !aligned16(packed_w) || !aligned16(y) || (bias && !aligned16(bias)))
+        return CTCONV_ERR_ALIGN;
+    if (route == CTCONV_ROUTE_POLYPHASE && !(polyphase_eligible(p) && polyphase_supported(p)) &&
+        !(p.N == 0 || p.H == 0 || p.W == 0))
+        return CTCONV_ERR_PARAM;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p.N == 0) return CTCONV_OK;
+    if (p.H == 0 || p.W == 0) return to_status(launch_fill(p, bias, y, s));  // no tap reaches y
+    if (route == CTCONV_ROUTE_AUTO) route = choose_route(p);
+    if (route == CTCONV_ROUTE_POLYPHASE) return to_status(launch_polyphase(p, x, packed_w, bias, y, s));
+    return to_status(launch_gather(p, x, packed_w, bias, y, s));
+}
+
+ctconv_status ctconv_forward(const void* x, const void* packed_w, const void* bias, void* y,
+                             int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                             const int64_t* in_spatial, const int64_t* kernel,
+                             const int64_t* stride, const int64_t* padding,
+                             const int64_t* output_padding, const int64_t* dilation,
+                             ctconv_dtype dtype, void* stream) {
+    return ctconv_forward_route(x, packed_w, bias, y, N, C_in, C_out, ndim, in_spatial, kernel,
+                                stride, padding, output_padding, dilation, dtype,
+                                CTCONV_ROUTE_AUTO, stream);
+}
+
+ctconv_status ctconv_elu(const void* x, void* y, int64_t n, ctconv_dtype dtype, void* stream) {
+    if (!x || !y) return CTCONV_ERR_NULL;
+    if (!dtype_ok(dtype)) return CTCONV_ERR_DTYPE;
+    if (n < 0) return CTCONV_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(y)) return CTCONV_ERR_ALIGN;
+    return to_status(launch_elu(x, y, n, dtype, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

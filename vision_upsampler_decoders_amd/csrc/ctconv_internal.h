@@ -1,0 +1,104 @@
+// Internal declarations shared by the ctconv HIP sources (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ctconv.h"
+
+namespace ctconv {
+
+// ---------------------------------------------------------------------------
+// Element types.  Storage is the raw 16/32-bit pattern; arithmetic is fp32.
+// ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+struct TBF16 {
+    using storage = uint16_t;
+    static constexpr int kVec = 8;  // elements per 16-byte fragment
+    __device__ static inline float to_f32(storage v) {
+        return __uint_as_float(static_cast<uint32_t>(v) << 16);
+    }
+    __device__ static inline storage from_f32(float f) {
+        // round to nearest even; NaN stays a quiet NaN
+        __bf16 b = static_cast<__bf16>(f);
+        return __builtin_bit_cast(uint16_t, b);
+    }
+};
+
+struct TF16 {
+    using storage = uint16_t;
+    static constexpr int kVec = 8;
+    __device__ static inline float to_f32(storage v) {
+        return static_cast<float>(__builtin_bit_cast(_Float16, v));
+    }
+    __device__ static inline storage from_f32(float f) {
+        return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));
+    }
+};
+
+struct TF32 {
+    using storage = float;
+    static constexpr int kVec = 4;
+    __device__ static inline float to_f32(storage v) { return v; }
+    __device__ static inline storage from_f32(float f) { return f; }
+};
+
+// ---------------------------------------------------------------------------
+// Normalised problem description (1-D problems use H = Ho = 1, kH = sH = 1,
+// pH = opH = 0, dH = 1).
+// ---------------------------------------------------------------------------
+struct Problem {
+    int ndim;
+    int64_t N, C_in, C_out;
+    int64_t H, W, Ho, Wo;
+    int64_t kH, kW, sH, sW, pH, pW, opH, opW, dH, dW;
+    int64_t mH, mW;   // taps per phase: ceil(k / s)
+    int64_t P, T;     // phases sH*sW, taps mH*mW
+    int64_t C_in_pad; // C_in rounded up to 32
+    ctconv_dtype dtype;
+};
+
+constexpr int64_t kCinAlign = 32;
+
+// Arguments of the polyphase MFMA kernel (filled by the host planner).
+struct PolyArgs {
+    const void* x;
+    const void* pw;
+    const void* bias;
+    void* y;
+    int64_t N, C_in, C_out, C_in_pad;
+    int64_t H, W, Ho, Wo;
+    int sy, sx, py, px;
+    int P, T;
+    int Ay, Ax;            // output rows per dimension in units of the stride
+    int dminy, dminx;      // floor(p / s)
+    int spready, spreadx;  // 1 when floor((b + p) / s) differs between phases
+    int WY, WX;            // x window per tile (rows x columns)
+    int TCO, PT;           // output channels and phases per column tile
+    int phase_subset;      // 0: a column tile holds every phase; 1: a run of PT phases
+    int n_ph_tiles, n_col_tiles;
+    int tiles_y, tiles_x;
+    int64_t n_row_tiles;
+    int n_chunks;          // C_in_pad / KC
+    int chunks_per_split;  // split over C_in: each blockIdx.y takes this many chunks
+    int atomic_out;        // 1: accumulate with fp32 atomics into a pre-filled y
+    int xcd_remap;         // 1: gridDim.x is a multiple of 8, remap for L2 locality
+};
+
+// Launchers (each returns hipGetLastError() of its launch).
+hipError_t launch_prepack(const Problem& p, const void* w, void* pw, hipStream_t s);
+hipError_t launch_gather(const Problem& p, const void* x, const void* pw, const void* bias,
+                         void* y, hipStream_t s);
+hipError_t launch_fill(const Problem& p, const void* bias, void* y, hipStream_t s);
+hipError_t launch_elu(const void* x, void* y, int64_t n, ctconv_dtype dt, hipStream_t s);
+
+// Polyphase planning and launch.  plan_polyphase returns false when no
+// compiled kernel instance covers the shape.
+bool polyphase_supported(const Problem& p);
+hipError_t launch_polyphase(const Problem& p, const void* x, const void* pw, const void* bias,
+                            void* y, hipStream_t s);
+
+}  // namespace ctconv

@@ -1,0 +1,244 @@
+"""ctypes binding of libctconv (include/ctconv.h), plus torch-tensor helpers.
+
+This module only marshals arguments: every step of the computation runs in
+the HIP kernels of libctconv.so.  Importing it fails loudly when the library
+has not been built; there is no CPU fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libctconv.so")
+
+CTCONV_F32, CTCONV_BF16, CTCONV_F16 = 0, 1, 2
+ROUTE_AUTO, ROUTE_POLYPHASE, ROUTE_GATHER = 0, 1, 2
+STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_PARAM", 4: "ERR_DTYPE",
+          5: "ERR_ALIGN", 6: "ERR_HIP"}
+
+EXPORTED = (
+    "ctconv_abi_version", "ctconv_status_string", "ctconv_output_shape", "ctconv_packed_bytes",
+    "ctconv_prepack", "ctconv_forward", "ctconv_forward_route", "ctconv_query_route",
+    "ctconv_elu",
+)
+
+
+class CtconvError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} "
+                         f"({_string(status) if _lib is not None else ''})")
+
+
+_lib = None
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def load(path: str = LIB_PATH):
+    """Load libctconv.so and declare its prototypes."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with "
+                          "`python -m vision_upsampler_decoders_amd.build`")
+    lib = ctypes.CDLL(path)
+    c_int, c_i64, c_vp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p
+    lib.ctconv_abi_version.argtypes = []
+    lib.ctconv_abi_version.restype = c_int
+    lib.ctconv_status_string.argtypes = [c_int]
+    lib.ctconv_status_string.restype = ctypes.c_char_p
+    lib.ctconv_output_shape.argtypes = [c_int] + [_i64p] * 7
+    lib.ctconv_output_shape.restype = c_int
+    lib.ctconv_packed_bytes.argtypes = [c_int, c_i64, c_i64, _i64p, _i64p, c_int,
+                                        ctypes.POINTER(ctypes.c_size_t)]
+    lib.ctconv_packed_bytes.restype = c_int
+    lib.ctconv_prepack.argtypes = [c_vp, c_vp, c_int, c_i64, c_i64, _i64p, _i64p, c_int, c_vp]
+    lib.ctconv_prepack.restype = c_int
+    fwd = [c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_int] + [_i64p] * 6 + [c_int]
+    lib.ctconv_forward.argtypes = fwd + [c_vp]
+    lib.ctconv_forward.restype = c_int
+    lib.ctconv_forward_route.argtypes = fwd + [c_int, c_vp]
+    lib.ctconv_forward_route.restype = c_int
+    lib.ctconv_query_route.argtypes = [c_i64, c_i64, c_i64, c_int] + [_i64p] * 6 + [
+        c_int, ctypes.POINTER(c_int)]
+    lib.ctconv_query_route.restype = c_int
+    lib.ctconv_elu.argtypes = [c_vp, c_vp, c_i64, c_int, c_vp]
+    lib.ctconv_elu.restype = c_int
+    _lib = lib
+    return lib
+
+
+def _string(status: int) -> str:
+    return _lib.ctconv_status_string(status).decode()
+
+
+def _arr(v: Sequence[int]):
+    return (ctypes.c_int64 * len(v))(*[int(t) for t in v])
+
+
+def per_dim(v, ndim: int) -> Tuple[int, ...]:
+    """Broadcast a scalar to every spatial dimension (as parse_hw does for 2-D)."""
+    if isinstance(v, int):
+        return (v,) * ndim
+    v = tuple(int(t) for t in v)
+    if len(v) != ndim:
+        raise ValueError(f"expected {ndim} values, got {v}")
+    return v
+
+
+def _check(fn: str, st: int):
+    if st != 0:
+        raise CtconvError(fn, st)
+
+
+# ---------------------------------------------------------------------------
+# Raw C-ABI calls with the same names (pointers and sizes only)
+# ---------------------------------------------------------------------------
+
+
+def ctconv_abi_version() -> int:
+    return load().ctconv_abi_version()
+
+
+def ctconv_status_string(status: int) -> str:
+    load()
+    return _string(status)
+
+
+def ctconv_output_shape(in_spatial, kernel, stride, padding=0, output_padding=0, dilation=1):
+    ndim = len(in_spatial)
+    out = (ctypes.c_int64 * ndim)()
+    st = load().ctconv_output_shape(ndim, _arr(in_spatial), _arr(per_dim(kernel, ndim)),
+                                    _arr(per_dim(stride, ndim)), _arr(per_dim(padding, ndim)),
+                                    _arr(per_dim(output_padding, ndim)),
+                                    _arr(per_dim(dilation, ndim)), out)
+    _check("ctconv_output_shape", st)
+    return tuple(int(v) for v in out)
+
+
+def ctconv_packed_bytes(ndim: int, C_in: int, C_out: int, kernel, stride, dtype: int) -> int:
+    nb = ctypes.c_size_t(0)
+    st = load().ctconv_packed_bytes(ndim, C_in, C_out, _arr(per_dim(kernel, ndim)),
+                                    _arr(per_dim(stride, ndim)), dtype, ctypes.byref(nb))
+    _check("ctconv_packed_bytes", st)
+    return int(nb.value)
+
+
+def ctconv_prepack(w_ptr: int, packed_ptr: int, ndim: int, C_in: int, C_out: int, kernel,
+                   stride, dtype: int, stream: int) -> None:
+    st = load().ctconv_prepack(w_ptr, packed_ptr, ndim, C_in, C_out,
+                               _arr(per_dim(kernel, ndim)), _arr(per_dim(stride, ndim)), dtype,
+                               stream)
+    _check("ctconv_prepack", st)
+
+
+def ctconv_forward_route(x_ptr: int, packed_ptr: int, bias_ptr: Optional[int], y_ptr: int, N: int,
+                         C_in: int, C_out: int, in_spatial, kernel, stride, padding,
+                         output_padding, dilation, dtype: int, route: int, stream: int) -> None:
+    ndim = len(in_spatial)
+    st = load().ctconv_forward_route(
+        x_ptr, packed_ptr, bias_ptr, y_ptr, N, C_in, C_out, ndim, _arr(in_spatial),
+        _arr(per_dim(kernel, ndim)), _arr(per_dim(stride, ndim)), _arr(per_dim(padding, ndim)),
+        _arr(per_dim(output_padding, ndim)), _arr(per_dim(dilation, ndim)), dtype, route, stream)
+    _check("ctconv_forward_route", st)
+
+
+def ctconv_forward(x_ptr: int, packed_ptr: int, bias_ptr: Optional[int], y_ptr: int, N: int,
+                   C_in: int, C_out: int, in_spatial, kernel, stride, padding, output_padding,
+                   dilation, dtype: int, stream: int) -> None:
+    ndim = len(in_spatial)
+    st = load().ctconv_forward(
+        x_ptr, packed_ptr, bias_ptr, y_ptr, N, C_in, C_out, ndim, _arr(in_spatial),
+        _arr(per_dim(kernel, ndim)), _arr(per_dim(stride, ndim)), _arr(per_dim(padding, ndim)),
+        _arr(per_dim(output_padding, ndim)), _arr(per_dim(dilation, ndim)), dtype, stream)
+    _check("ctconv_forward", st)
+
+
+def ctconv_query_route(N: int, C_in: int, C_out: int, in_spatial, kernel, stride, padding=0,
+                       output_padding=0, dilation=1, dtype: int = CTCONV_F32) -> int:
+    ndim = len(in_spatial)
+    r = ctypes.c_int(-1)
+    st = load().ctconv_query_route(
+        N, C_in, C_out, ndim, _arr(in_spatial), _arr(per_dim(kernel, ndim)),
+        _arr(per_dim(stride, ndim)), _arr(per_dim(padding, ndim)),
+        _arr(per_dim(output_padding, ndim)), _arr(per_dim(dilation, ndim)), dtype,
+        ctypes.byref(r))
+    _check("ctconv_query_route", st)
+    return r.value
+
+
+def ctconv_elu(x_ptr: int, y_ptr: int, n: int, dtype: int, stream: int) -> None:
+    _check("ctconv_elu", load().ctconv_elu(x_ptr, y_ptr, n, dtype, stream))
+
+
+# ---------------------------------------------------------------------------
+# torch helpers (device memory and streams only)
+# ---------------------------------------------------------------------------
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: CTCONV_F32, torch.bfloat16: CTCONV_BF16, torch.float16: CTCONV_F16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def prepack(w, stride, stream=None):
+    """Packed phase-major copy of a ConvTranspose weight w [C_in, C_out, k...] (device)."""
+    torch = _torch()
+    if not w.is_cuda:
+        raise ValueError("w must be a device tensor")
+    w = w.contiguous()
+    ndim = w.dim() - 2
+    C_in, C_out = w.shape[0], w.shape[1]
+    k = tuple(w.shape[2:])
+    dt = dtype_code(w)
+    nb = ctconv_packed_bytes(ndim, C_in, C_out, k, stride, dt)
+    packed = torch.empty(nb // w.element_size(), dtype=w.dtype, device=w.device)
+    ctconv_prepack(w.data_ptr(), packed.data_ptr(), ndim, C_in, C_out, k, stride, dt,
+                   _stream(stream))
+    return packed
+
+
+def forward(x, packed, bias, C_out: int, kernel, stride, padding=0, output_padding=0,
+            dilation=1, route: int = ROUTE_AUTO, out=None, stream=None):
+    """y = ConvTranspose(x, w, bias) with w given by its packed form (device tensors)."""
+    torch = _torch()
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
+    x = x.contiguous()
+    ndim = x.dim() - 2
+    N, C_in = x.shape[0], x.shape[1]
+    sp = tuple(x.shape[2:])
+    osp = ctconv_output_shape(sp, kernel, stride, padding, output_padding, dilation)
+    y = out if out is not None else torch.empty((N, C_out) + osp, dtype=x.dtype, device=x.device)
+    bptr = None if bias is None else bias.contiguous().data_ptr()
+    ctconv_forward_route(x.data_ptr(), packed.data_ptr(), bptr, y.data_ptr(), N, C_in, C_out, sp,
+                         kernel, stride, padding, output_padding, dilation, dtype_code(x), route,
+                         _stream(stream))
+    return y
+
+
+def elu(x, out=None, stream=None):
+    torch = _torch()
+    x = x.contiguous()
+    y = out if out is not None else torch.empty_like(x)
+    ctconv_elu(x.data_ptr(), y.data_ptr(), x.numel(), dtype_code(x), _stream(stream))
+    return y
