@@ -46,8 +46,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="vocoder_stack")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-frames", type=int, default=150,
-                    help="input frames of one batch item for the oracle's timed sample")
+    ap.add_argument("--cpu-items", type=int, default=2,
+                    help="batch items of the workload in the oracle's timed sample")
+    ap.add_argument("--cpu-frames", type=int, default=0,
+                    help="leading input frames per item in the sample (0: all)")
     return ap.parse_args()
 
 
@@ -96,32 +98,37 @@ def load_traffic(workload):
     return None
 
 
-def cpu_baseline(wl, frames):
-    """The oracle, as it stands, on one batch item and the first `frames` input
-    positions of the workload (every layer, and the ELUs of the stack)."""
+def cpu_baseline(wl, items, frames):
+    """The oracle, as it stands, on the first `items` batch items of the
+    workload (leading `frames` input positions when frames > 0), every layer
+    and the ELUs of the stack."""
     import oracle
     from synth import inputs as I
 
     sp = tuple(wl.in_spatial)
-    if len(sp) == 1:
+    items = max(1, min(items, wl.N))
+    if frames <= 0:
+        sub = sp
+    elif len(sp) == 1:
         sub = (min(frames, sp[0]),)
     else:  # 2-D: a band of rows
-        sub = (max(1, min(sp[0], frames // 8)), sp[1])
-    x = I.gen_x(wl, N=1, in_spatial=sub)
+        sub = (max(1, min(sp[0], frames)), sp[1])
+    x = I.gen_x(wl, N=wl.N, in_spatial=sp)[:items]
+    x = x[(slice(None), slice(None)) + tuple(slice(0, v) for v in sub)]
     ws = [I.gen_w(wl, li) for li in range(len(wl.layers))]
     bs = [I.gen_bias(wl, li) for li in range(len(wl.layers))]
     flops = 0
     t0 = time.perf_counter()
     cur = x
     for li, L in enumerate(wl.layers):
-        flops += 2 * L.C_in * L.C_out * int(np.prod(L.kernel)) * int(np.prod(cur.shape[2:]))
+        flops += 2 * items * L.C_in * L.C_out * int(np.prod(L.kernel)) * int(np.prod(cur.shape[2:]))
         cur = oracle.conv_transpose(cur, ws[li], bs[li], L.stride, L.padding,
                                     L.output_padding, L.dilation)
         if wl.elu_between and li + 1 < len(wl.layers):
             cur = oracle.elu(cur)
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"batch item 0, input {list(sub)} of {list(sp)}, all {len(wl.layers)} "
+            "sample": f"batch items 0..{items - 1} of {wl.N}, input {list(sub)} of {list(sp)}, all {len(wl.layers)} "
                       f"layer(s){' with ELU between' if wl.elu_between else ''}; "
                       f"{flops / 1e9:.2f} GFLOP in {dt:.2f} s, single-threaded float64",
             "seconds": dt, "host_nproc": os.cpu_count()}
@@ -166,26 +173,39 @@ def main():
         del w
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    sptr = int(stream.cuda_stream)
+    dcode = {"f32": 0, "bf16": 1, "f16": 2}[wl.dtype]
 
     n_layers = len(geo)
+    # arguments marshalled once per layer: each launch is one foreign call
+    convs = [C.Conv(wl.N, L.C_in, L.C_out, sp, L.kernel, L.stride, L.padding, L.output_padding,
+                    L.dilation, dcode) for (L, sp, osp, _, _) in geo]
+    ptrs = []
+    cur_ptr = x.data_ptr()
+    for li in range(n_layers):
+        b = biases[li]
+        ptrs.append((cur_ptr, packed[li].data_ptr(), None if b is None else b.data_ptr(),
+                     outs[li].data_ptr()))
+        cur_ptr = outs[li].data_ptr()
+        if elus[li] is not None:
+            cur_ptr = elus[li].data_ptr()
+    elu_fn = C.load().ctconv_elu
 
     def step(ev=None):
-        cur = x
-        for li, (L, sp, osp, _, _) in enumerate(geo):
+        for li in range(n_layers):
             if ev is not None:
                 ev[li][0].record(stream)
-            C.forward(cur, packed[li], biases[li], L.C_out, L.kernel, L.stride, L.padding,
-                      L.output_padding, L.dilation, out=outs[li])
+            convs[li](*ptrs[li], sptr)
             if ev is not None:
                 ev[li][1].record(stream)
-            cur = outs[li]
             if elus[li] is not None:
                 if ev is not None:
                     ev[n_layers + li][0].record(stream)
-                C.elu(cur, out=elus[li])
+                st = elu_fn(outs[li].data_ptr(), elus[li].data_ptr(), outs[li].numel(), dcode, sptr)
+                if st != 0:
+                    raise C.CtconvError("ctconv_elu", st)
                 if ev is not None:
                     ev[n_layers + li][1].record(stream)
-                cur = elus[li]
 
     for _ in range(args.warmup):
         step()
@@ -280,7 +300,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_frames)
+        res["cpu_baseline"] = cpu_baseline(wl, args.cpu_items, args.cpu_frames)
     print(json.dumps(res), flush=True)
 
 

@@ -112,12 +112,14 @@ ctconv_status ctconv_prepack(const void* w, void* packed_w, int ndim, int64_t C_
 
 /*
  * y = ConvTranspose(x, w, bias) on the device.
- *   x          device, [N, C_in, in_spatial...]
+ *   x          device, [N, C_in, in_spatial...]; may be NULL when it has no
+ *              element (N = 0 or an input size of 0)
  *   packed_w   device, written by ctconv_prepack with the same C_in, C_out,
  *              kernel, stride and dtype (a precondition the library cannot check)
  *   bias       device [C_out], or NULL for none
  *   y          device, [N, C_out, out_spatial...] (see ctconv_output_shape);
- *              every element is written.  Must not overlap x, packed_w or bias.
+ *              every element is written (outputs no tap reaches get the bias,
+ *              or 0).  Must not overlap x, packed_w or bias.  May be NULL when N = 0.
  *   N >= 0, C_in >= 1, C_out >= 1; other arguments as in ctconv_output_shape.
  * Pointers must be 16-byte aligned.  With N = 0 nothing is enqueued.
  */

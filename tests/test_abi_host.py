@@ -116,6 +116,10 @@ def _fwd(lib, x=0x1000, w=0x2000, b=None, y=0x3000, N=1, C_in=4, C_out=4, sp=(8,
 def test_forward_validation_before_launch(lib):
     # Every call below must be rejected on the host: none reaches a launch.
     assert _fwd(lib, x=None) == 1
+    # an empty input may come with a NULL pointer (it is never read); its
+    # output is then only filled, which would launch, so check N = 0 only
+    assert _fwd(lib, x=None, y=None, N=0) == 0
+    assert _fwd(lib, y=None, sp=(0,), k=8, s=2, p=0) == 1
     assert _fwd(lib, w=None) == 1
     assert _fwd(lib, y=None) == 1
     assert _fwd(lib, C_in=0) == 2

@@ -216,7 +216,6 @@ ctconv_status ctconv_forward_route(const void* x, const void* packed_w, const vo
                                    const int64_t* stride, const int64_t* padding,
                                    const int64_t* output_padding, const int64_t* dilation,
                                    ctconv_dtype dtype, ctconv_route route, void* stream) {
-    if (!x || !packed_w || !y) return CTCONV_ERR_NULL;
     if (route != CTCONV_ROUTE_AUTO && route != CTCONV_ROUTE_POLYPHASE &&
         route != CTCONV_ROUTE_GATHER)
         return CTCONV_ERR_PARAM;
@@ -224,7 +223,11 @@ ctconv_status ctconv_forward_route(const void* x, const void* packed_w, const vo
     const ctconv_status st = build_problem(N, C_in, C_out, ndim, in_spatial, kernel, stride,
                                            padding, output_padding, dilation, dtype, &p);
     if (st != CTCONV_OK) return st;
-    if (!aligned16(x) || !aligned16(packed_w) || !aligned16(y) || (bias && !aligned16(bias)))
+    // x may be NULL when it holds no element, y when N = 0 (empty tensors)
+    const bool x_empty = p.N == 0 || p.H == 0 || p.W == 0;
+    if (!packed_w || (!x && !x_empty) || (!y && p.N != 0)) return CTCONV_ERR_NULL;
+    if ((x && !aligned16(x)) || !aligned16(packed_w) || (y && !aligned16(y)) ||
+        (bias && !aligned16(bias)))
         return CTCONV_ERR_ALIGN;
     if (route == CTCONV_ROUTE_POLYPHASE && !(polyphase_eligible(p) && polyphase_supported(p)) &&
         !(p.N == 0 || p.H == 0 || p.W == 0))

@@ -51,12 +51,18 @@ namespace ctconv {
 
 namespace {
 
+// Fragments live in registers as native 4 x 32-bit vectors (16 bytes); the
+// 1-byte-aligned variant gives plain, possibly unaligned, 16-byte accesses.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_u __attribute__((ext_vector_type(4), aligned(1)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
 template <class TR>
 struct Mma;
 
 template <>
 struct Mma<TBF16> {
-    __device__ static inline void step(f32x4& acc, const uint4& a, const uint4& b) {
+    __device__ static inline void step(f32x4& acc, const u32x4 a, const u32x4 b) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                       __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
     }
@@ -64,7 +70,7 @@ struct Mma<TBF16> {
 
 template <>
 struct Mma<TF16> {
-    __device__ static inline void step(f32x4& acc, const uint4& a, const uint4& b) {
+    __device__ static inline void step(f32x4& acc, const u32x4 a, const u32x4 b) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                      __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
     }
@@ -75,17 +81,70 @@ struct Mma<TF32> {
     // Lane group g holds channels 4g..4g+3 of the 16-channel step in one
     // 16-byte fragment; MFMA number e consumes element e of every group, so
     // the four MFMAs together reduce over all 16 channels.
-    __device__ static inline void step(f32x4& acc, const uint4& a, const uint4& b) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x),
+    __device__ static inline void step(f32x4& acc, const u32x4 a, const u32x4 b) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[0]), __uint_as_float(b[0]),
                                                    acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y),
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[1]), __uint_as_float(b[1]),
                                                    acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z),
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[2]), __uint_as_float(b[2]),
                                                    acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w),
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[3]), __uint_as_float(b[3]),
                                                    acc, 0, 0, 0);
     }
 };
+
+__device__ inline u32x4 load16_unaligned(const void* p) {
+    return *reinterpret_cast<const u32x4_u*>(p);
+}
+
+__device__ inline void store16_unaligned(void* p, const u32x4 v) {
+    *reinterpret_cast<u32x4_u*>(p) = v;
+}
+
+// VEC elements of one row at clamped positions p0 .. p0+VEC-1 (edge tiles).
+template <typename S>
+__device__ inline u32x4 load_row_clamped(const S* rowp, int p0, int W) {
+    if constexpr (sizeof(S) == 2) {
+        u16x8 v;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            int pos = p0 + p;
+            pos = pos < 0 ? 0 : (pos >= W ? W - 1 : pos);
+            v[p] = rowp[pos];
+        }
+        return __builtin_bit_cast(u32x4, v);
+    } else {
+        u32x4 v;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            int pos = p0 + p;
+            pos = pos < 0 ? 0 : (pos >= W ? W - 1 : pos);
+            v[p] = __builtin_bit_cast(uint32_t, rowp[pos]);
+        }
+        return __builtin_bit_cast(u32x4, v);
+    }
+}
+
+// 8x8 transpose of 16-bit elements held as eight 16-byte rows: out[p] holds
+// element p of in[0..7] (v_perm_b32 gathers one half-word from each of two
+// rows per output dword).
+__device__ inline void transpose8x16(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const unsigned sel = (p & 1) ? 0x07060302u : 0x05040100u;
+        u32x4 d;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            d[c] = __builtin_amdgcn_perm(in[2 * c + 1][p >> 1], in[2 * c][p >> 1], sel);
+        out[p] = d;
+    }
+}
+
+// 4x4 transpose of 32-bit elements (register renaming only).
+__device__ inline void transpose4x32(const u32x4 (&in)[4], u32x4 (&out)[4]) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) out[p] = u32x4{in[0][p], in[1][p], in[2][p], in[3][p]};
+}
 
 template <class TR, int MY, int MX, int TAX, int RB, int CB, int WM, int WN, int KS>
 struct Cfg {
@@ -99,26 +158,32 @@ struct Cfg {
     static constexpr int BN = WN * CB * 16;
     static constexpr int TAY = BM / TAX;
     static constexpr int T = MY * MX;
-    static constexpr int WYM = TAY + MY - 1 + (TAY > 1 ? 1 : 0);
-    static constexpr int WXM = TAX + MX;
-    static constexpr int XROWS = WYM * WXM;
+    static constexpr int WYM = TAY + MY - 1 + (TAY > 1 ? 1 : 0);  // window rows (max)
+    static constexpr int WXP = (TAX + MX + VEC - 1) / VEC * VEC;  // window columns, padded
+    static constexpr int XROWS = WYM * WXP;
     static constexpr int BROWS = T * BN;
     static constexpr int STAGE = (XROWS + BROWS) * RSA;
-    static constexpr int NG = KC / VEC;
-    static constexpr int XITEMS = (XROWS * NG + 255) / 256;
-    static constexpr int BITEMS = (BROWS * NG + 255) / 256;
-    static constexpr int SMEM = (2 * STAGE > BM * BN ? 2 * STAGE : BM * BN);
+    static constexpr int NG = KC / VEC;                           // channel groups per chunk
+    static constexpr int NW = WM * WN;                            // waves per workgroup
+    static constexpr int NT = 64 * NW;                            // threads per workgroup
+    // load items are split into NW contiguous per-wave ranges (coalesced lanes)
+    static constexpr int XMAX = WYM * (WXP / VEC) * NG;
+    static constexpr int XITEMS = ((XMAX + NW - 1) / NW + 63) / 64;
+    static constexpr int BMAX = BROWS * NG;
+    static constexpr int BITEMS = ((BMAX + NW - 1) / NW + 63) / 64;
+    static constexpr int EPI = BM * BN + BN * VEC;  // staged output tile, padded
+    static constexpr int SMEM = (2 * STAGE > EPI ? 2 * STAGE : EPI);
     static_assert(BM % TAX == 0 && TAX % 16 == 0, "tile rows");
-    static_assert(WM * WN == 4, "four waves");
+    static_assert(NW == 4 || NW == 8, "four or eight waves");
     static_assert(SMEM * ES <= 160 * 1024, "LDS");
 };
 
 template <class TR, int MY, int MX, int TAX, int RB, int CB, int WM, int WN, int KS>
-__global__ __launch_bounds__(256) void poly_kernel(const PolyArgs a) {
+__global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
     using C = Cfg<TR, MY, MX, TAX, RB, CB, WM, WN, KS>;
     using S = typename TR::storage;
     constexpr int VEC = C::VEC, KC = C::KC, RSA = C::RSA, BN = C::BN, T = C::T;
-    constexpr int NG = C::NG;
+    constexpr int NG = C::NG, WXP = C::WXP;
 
     __shared__ __attribute__((aligned(16))) S smem[C::SMEM];
 
@@ -140,44 +205,61 @@ __global__ __launch_bounds__(256) void poly_kernel(const PolyArgs a) {
     const int co0 = (col_tile / a.n_ph_tiles) * a.TCO;
     const int b0 = (col_tile % a.n_ph_tiles) * a.PT;
     const int ay0 = ty_t * C::TAY, ax0 = tx_t * TAX;
-    const int64_t wy0 = (int64_t)ay0 + a.dminy - (MY - 1);
-    const int64_t wx0 = (int64_t)ax0 + a.dminx - (MX - 1);
+    const int wy0 = ay0 + a.dminy - (MY - 1);
+    const int wx0 = ax0 + a.dminx - (MX - 1);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
     const int li = lane & 15, lg = lane >> 4;
 
-    // ---- per-thread load descriptors (fixed across chunks) ----------------
+    // ---- x staging descriptors: item = (window row, VEC positions, VEC channels)
     const int64_t HW = a.H * a.W;
-    const int npos = a.WY * a.WX;
-    const int xitems = npos * NG;
-    int64_t xsp[C::XITEMS];   // spatial offset, -1 when outside the input
-    int xch[C::XITEMS];       // channel offset of the group within a chunk
-    int xlds[C::XITEMS];      // LDS element offset (-1: no item)
+    const int ngx = WXP / VEC;
+    const int xitems = a.WY * ngx * NG;
+    const int xper = (xitems + C::NW - 1) / C::NW;  // items per wave
+    int xrow[C::XITEMS];   // element offset of (row iy, position P0) within a channel plane
+    int xp0[C::XITEMS];    // first position P0 (may be negative)
+    int xg0[C::XITEMS];    // channel offset of the group within a chunk
+    int xlds[C::XITEMS];   // LDS element offset of the first position row (-1: no item)
+    bool xrowok[C::XITEMS];
 #pragma unroll
     for (int it = 0; it < C::XITEMS; ++it) {
-        const int q = tid + 256 * it;
+        const int qw = lane + 64 * it;
+        const int q = wave * xper + qw;
         xlds[it] = -1;
-        xsp[it] = -1;
-        xch[it] = 0;
-        if (q < xitems) {
-            const int pos = q % npos, g = q / npos;
-            const int64_t iy = wy0 + pos / a.WX, ix = wx0 + pos % a.WX;
-            if (iy >= 0 && iy < a.H && ix >= 0 && ix < a.W) xsp[it] = iy * a.W + ix;
-            xch[it] = g * VEC;
-            xlds[it] = pos * RSA + g * VEC;
+        xrow[it] = 0;
+        xp0[it] = 0;
+        xg0[it] = 0;
+        xrowok[it] = false;
+        if (qw < xper && q < xitems) {
+            // channel group fastest: lanes g = 0..NG-1 of one position group write
+            // adjacent 16-byte slots of the same LDS rows (at most 2-way bank
+            // conflicts), while the lanes sharing a g still read 16-byte runs
+            // that are contiguous along the spatial axis
+            const int g = q % NG;
+            const int r2 = q / NG;
+            const int gx = r2 % ngx;
+            const int wy = r2 / ngx;
+            const int iy = wy0 + wy;
+            xrowok[it] = iy >= 0 && iy < a.H;
+            xp0[it] = wx0 + gx * VEC;
+            xrow[it] = (xrowok[it] ? iy : 0) * (int)a.W;
+            xg0[it] = g * VEC;
+            xlds[it] = (wy * WXP + gx * VEC) * RSA + g * VEC;
         }
     }
     const S* xn = xg + n * a.C_in * HW;
 
     int64_t boff[C::BITEMS];  // packed-weight element offset, -1 for a zero row
     int blds[C::BITEMS];
+    constexpr int bper = (C::BMAX + C::NW - 1) / C::NW;
 #pragma unroll
     for (int it = 0; it < C::BITEMS; ++it) {
-        const int q = tid + 256 * it;
+        const int qw = lane + 64 * it;
+        const int q = wave * bper + qw;
         boff[it] = -1;
         blds[it] = -1;
-        if (q < C::BROWS * NG) {
+        if (qw < bper && q < C::BMAX) {
             const int row = q / NG, piece = q % NG;
             const int r = row / BN, tc = row % BN;
             const int pb = tc / a.TCO, co = co0 + tc % a.TCO, b = b0 + pb;
@@ -190,54 +272,96 @@ __global__ __launch_bounds__(256) void poly_kernel(const PolyArgs a) {
         }
     }
 
-    // ---- per-wave column-block phase shifts -------------------------------
+    // ---- per-wave column-block phase shifts (wave-uniform, kept in SGPRs) --
     int ddy[CB], ddx[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         const int tc0 = (wn * CB + cb) * 16;
         const int pb = tc0 / a.TCO, b = b0 + pb;
-        ddy[cb] = 0;
-        ddx[cb] = 0;
+        int dy = 0, dx = 0;
         if (pb < a.PT && b < a.P) {
             const int by = b / a.sx, bx = b % a.sx;
-            ddy[cb] = (by + a.py) / a.sy - a.dminy;
-            ddx[cb] = (bx + a.px) / a.sx - a.dminx;
+            dy = (by + a.py) / a.sy - a.dminy;
+            dx = (bx + a.px) / a.sx - a.dminx;
         }
+        ddy[cb] = __builtin_amdgcn_readfirstlane(dy);
+        ddx[cb] = __builtin_amdgcn_readfirstlane(dx);
     }
 
-    uint4 xr[C::XITEMS];
-    uint4 br[C::BITEMS];
+    u32x4 xr[C::XITEMS][VEC];
+    uint32_t xmask[C::XITEMS];  // bit p: position p valid; bit 8+e: channel e valid
+    u32x4 br[C::BITEMS];
 
-    auto gload = [&](int c) {
+    // Global -> registers.  Loads only: nothing here consumes a loaded value,
+    // so the loads of chunk c+1 stay in flight while chunk c is computed.
+    auto gload = [&](int c) __attribute__((always_inline)) {
         const int cbase = c * KC;
 #pragma unroll
         for (int it = 0; it < C::XITEMS; ++it) {
-            S v[VEC];
-            const int ch = cbase + xch[it];
+            xmask[it] = 0;
+            if (xlds[it] < 0) continue;
+            const int p0 = xp0[it];
+            const bool inside = p0 >= 0 && p0 + VEC <= a.W;
+            uint32_t m = 0;
+#pragma unroll
+            for (int p = 0; p < VEC; ++p)
+                m |= (xrowok[it] && p0 + p >= 0 && p0 + p < a.W) ? (1u << p) : 0u;
+            const int ch0 = cbase + xg0[it];
+            const S* base = xn + (int64_t)ch0 * HW + xrow[it];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                v[e] = S(0);
-                if (xsp[it] >= 0 && ch + e < a.C_in) v[e] = xn[(int64_t)(ch + e) * HW + xsp[it]];
+                const bool chok = ch0 + e < a.C_in;
+                m |= chok ? (1u << (8 + e)) : 0u;
+                const S* rowp = chok ? base + (int64_t)e * HW : xn + xrow[it];
+                // clamped in-row addresses at the edges; masked at LDS store time
+                xr[it][e] = inside ? load16_unaligned(rowp + p0)
+                                   : load_row_clamped(rowp, p0, (int)a.W);
             }
-            xr[it] = *reinterpret_cast<const uint4*>(v);
+            xmask[it] = m;
         }
 #pragma unroll
         for (int it = 0; it < C::BITEMS; ++it) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (boff[it] >= 0) v = *reinterpret_cast<const uint4*>(pwg + boff[it] + cbase);
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (boff[it] >= 0) v = *reinterpret_cast<const u32x4*>(pwg + boff[it] + cbase);
             br[it] = v;
         }
     };
 
-    auto lstore = [&](int st) {
+    auto lstore = [&](int st) __attribute__((always_inline)) {
         S* xs = smem + st * C::STAGE;
         S* bs = xs + C::XROWS * RSA;
+        const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int it = 0; it < C::XITEMS; ++it)
-            if (xlds[it] >= 0) *reinterpret_cast<uint4*>(xs + xlds[it]) = xr[it];
+        for (int it = 0; it < C::XITEMS; ++it) {
+            if (xlds[it] < 0) continue;
+            const uint32_t m = xmask[it];
+            constexpr uint32_t kAll = (1u << (8 + VEC)) - (1u << 8) + (1u << VEC) - 1u;
+            u32x4 in[VEC], tr[VEC];
+            if (m == kAll) {  // every position and channel valid: no masking
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) in[e] = xr[it][e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) in[e] = (m & (1u << (8 + e))) ? xr[it][e] : z;
+            }
+            if constexpr (VEC == 8)
+                transpose8x16(in, tr);
+            else
+                transpose4x32(in, tr);
+            if (m == kAll) {
+#pragma unroll
+                for (int p = 0; p < VEC; ++p)
+                    *reinterpret_cast<u32x4*>(xs + xlds[it] + p * RSA) = tr[p];
+            } else {
+#pragma unroll
+                for (int p = 0; p < VEC; ++p)
+                    *reinterpret_cast<u32x4*>(xs + xlds[it] + p * RSA) =
+                        (m & (1u << p)) ? tr[p] : z;
+            }
+        }
 #pragma unroll
         for (int it = 0; it < C::BITEMS; ++it)
-            if (blds[it] >= 0) *reinterpret_cast<uint4*>(bs + blds[it]) = br[it];
+            if (blds[it] >= 0) *reinterpret_cast<u32x4*>(bs + blds[it]) = br[it];
     };
 
     f32x4 acc[RB][CB];
@@ -251,49 +375,59 @@ __global__ __launch_bounds__(256) void poly_kernel(const PolyArgs a) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const int tr0 = (wm * RB + rb) * 16;
-        arow[rb] = (tr0 / TAX) * a.WX + (tr0 % TAX) + li;
+        arow[rb] = (tr0 / TAX) * WXP + (tr0 % TAX) + li;
     }
+    const int bcol = (wn * CB) * 16 + li;
 
-    auto compute = [&](int st) {
+    // Shift bookkeeping: column block cb belongs to class (dd_y, dd_x) with
+    // dd in {0, 1} per dimension; for tap (ry, rx) its A rows sit at window
+    // offset (dd_y + MY-1-ry, dd_x + MX-1-rx).  Per tap, the B fragments of all
+    // column blocks are loaded, then for every class present in this wave the
+    // A fragments at that class's offset, then the MFMAs of the class's
+    // column blocks.  Classes and their presence mask are wave-uniform.
+    constexpr bool Y2 = C::TAY > 1;  // 2-D tile: the row offset may differ too
+    int cls[CB];
+    uint32_t clsmask = 0;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        cls[cb] = (Y2 ? ddy[cb] * 2 : 0) + ddx[cb];
+        clsmask |= 1u << cls[cb];
+    }
+    auto compute = [&](int st) __attribute__((always_inline)) {
         const S* xs = smem + st * C::STAGE;
         const S* bs = xs + C::XROWS * RSA;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int kofs = ks * C::KSTEP + lg * VEC;
-            uint4 bfr[CB][T];
 #pragma unroll
-            for (int cb = 0; cb < CB; ++cb)
+            for (int ry = 0; ry < MY; ++ry)
 #pragma unroll
-                for (int r = 0; r < T; ++r)
-                    bfr[cb][r] = *reinterpret_cast<const uint4*>(
-                        bs + (r * BN + (wn * CB + cb) * 16 + li) * RSA + kofs);
+                for (int rx = 0; rx < MX; ++rx) {
+                    const int r = ry * MX + rx;
+                    u32x4 bfr[CB];
 #pragma unroll
-            for (int ey = 0; ey <= MY; ++ey) {
-                if (ey == MY && !a.spready) continue;
+                    for (int cb = 0; cb < CB; ++cb)
+                        bfr[cb] = *reinterpret_cast<const u32x4*>(
+                            bs + (r * BN + bcol + cb * 16) * RSA + kofs);
 #pragma unroll
-                for (int ex = 0; ex <= MX; ++ex) {
-                    if (ex == MX && !a.spreadx) continue;
-                    uint4 afr[RB];
+                    for (int c = 0; c < (Y2 ? 4 : 2); ++c) {
+                        if (!(clsmask & (1u << c))) continue;
+                        const int ey = (c >> 1) + MY - 1 - ry;
+                        const int ex = (c & 1) + MX - 1 - rx;
+                        u32x4 afr[RB];
 #pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-                        afr[rb] = *reinterpret_cast<const uint4*>(
-                            xs + (arow[rb] + ey * a.WX + ex) * RSA + kofs);
+                        for (int rb = 0; rb < RB; ++rb)
+                            afr[rb] = *reinterpret_cast<const u32x4*>(
+                                xs + (arow[rb] + ey * WXP + ex) * RSA + kofs);
 #pragma unroll
-                    for (int cb = 0; cb < CB; ++cb) {
-                        const int ry = ddy[cb] + MY - 1 - ey;
-                        const int rx = ddx[cb] + MX - 1 - ex;
+                        for (int cb = 0; cb < CB; ++cb)
+                            if (cls[cb] == c) {
 #pragma unroll
-                        for (int ryc = 0; ryc < MY; ++ryc)
-#pragma unroll
-                            for (int rxc = 0; rxc < MX; ++rxc)
-                                if (ryc == ry && rxc == rx) {
-#pragma unroll
-                                    for (int rb = 0; rb < RB; ++rb)
-                                        Mma<TR>::step(acc[rb][cb], afr[rb], bfr[cb][ryc * MX + rxc]);
-                                }
+                                for (int rb = 0; rb < RB; ++rb)
+                                    Mma<TR>::step(acc[rb][cb], afr[rb], bfr[cb]);
+                            }
                     }
                 }
-            }
         }
     };
 
@@ -317,16 +451,21 @@ __global__ __launch_bounds__(256) void poly_kernel(const PolyArgs a) {
     const S* __restrict__ biasg = static_cast<const S*>(a.bias);
     const int R = a.phase_subset ? TAX : C::TAY * a.sy;
     const int SS = a.phase_subset ? a.PT : TAX * a.sx;
+    // output-channel stride padded by 16 bytes: lanes of one MFMA column block
+    // hold consecutive output channels, so an unpadded power-of-two stride
+    // would put all 16 of their staging writes in one LDS bank
+    const int CSTR = R * SS + VEC;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int cb = 0; cb < CB; ++cb) {
+        const int tc = bcol + cb * 16;
+        const int pb = tc / a.TCO, co_l = tc - (tc / a.TCO) * a.TCO;
+        if (pb >= a.PT) continue;
+        const int co = co0 + co_l;
+        float bv = 0.f;
+        if (!a.atomic_out && biasg != nullptr && co < a.C_out) bv = TR::to_f32(biasg[co]);
+        const int by = pb / a.sx, bx = pb - by * a.sx;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            const int tc = (wn * CB + cb) * 16 + li;
-            const int pb = tc / a.TCO, co_l = tc % a.TCO;
-            if (pb >= a.PT) continue;
-            const int co = co0 + co_l;
-            float bv = 0.f;
-            if (!a.atomic_out && biasg != nullptr && co < a.C_out) bv = TR::to_f32(biasg[co]);
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int tr = (wm * RB + rb) * 16 + lg * 4 + i;
@@ -336,37 +475,53 @@ __global__ __launch_bounds__(256) void poly_kernel(const PolyArgs a) {
                     rr = axl;
                     ss = pb;
                 } else {
-                    rr = ayl * a.sy + pb / a.sx;
-                    ss = axl * a.sx + pb % a.sx;
+                    rr = ayl * a.sy + by;
+                    ss = axl * a.sx + bx;
                 }
-                smem[(co_l * R + rr) * SS + ss] = TR::from_f32(acc[rb][cb][i] + bv);
+                smem[co_l * CSTR + rr * SS + ss] = TR::from_f32(acc[rb][cb][i] + bv);
             }
-        }
+    }
     __syncthreads();
 
     S* __restrict__ yg = static_cast<S*>(a.y);
-    const int total = a.TCO * R * SS;
-    for (int e = tid; e < total; e += 256) {
-        const int ss = e % SS;
-        const int rr = (e / SS) % R;
-        const int co = co0 + e / (SS * R);
+    const int nrows = a.TCO * R;
+    const bool vec_ok = (SS % VEC) == 0 && !a.atomic_out;
+    for (int row = wave; row < nrows; row += C::NW) {
+        const int co_l = row / R, rr = row - (row / R) * R;
+        const int co = co0 + co_l;
         if (co >= a.C_out) continue;
-        int64_t oy, ox;
+        int64_t oy, ox0;
+        int lim;  // valid elements of this staged row
         if (a.phase_subset) {
-            const int b = b0 + ss;
-            if (b >= a.P) continue;
             oy = 0;
-            ox = (int64_t)(ax0 + rr) * a.sx + b;
+            ox0 = (int64_t)(ax0 + rr) * a.sx + b0;
+            lim = min(SS, a.P - b0);
+            if (ox0 >= a.Wo) continue;
+            if (ox0 + lim > a.Wo) lim = (int)(a.Wo - ox0);
         } else {
             oy = (int64_t)ay0 * a.sy + rr;
-            ox = (int64_t)ax0 * a.sx + ss;
+            ox0 = (int64_t)ax0 * a.sx;
+            if (oy >= a.Ho || ox0 >= a.Wo) continue;
+            lim = (int)min((int64_t)SS, a.Wo - ox0);
         }
-        if (oy >= a.Ho || ox >= a.Wo) continue;
-        const int64_t idx = ((n * a.C_out + co) * a.Ho + oy) * a.Wo + ox;
-        if (a.atomic_out)
-            atomicAdd(reinterpret_cast<float*>(yg) + idx, TR::to_f32(smem[e]));
-        else
-            yg[idx] = smem[e];
+        const int64_t gbase = ((n * a.C_out + co) * a.Ho + oy) * a.Wo + ox0;
+        const S* srow = smem + co_l * CSTR + rr * SS;
+        if (vec_ok) {
+            for (int s0 = lane * VEC; s0 < lim; s0 += 64 * VEC) {
+                if (s0 + VEC <= lim) {
+                    store16_unaligned(yg + gbase + s0, *reinterpret_cast<const u32x4*>(srow + s0));
+                } else {
+                    for (int e = s0; e < lim; ++e) yg[gbase + e] = srow[e];
+                }
+            }
+        } else {
+            for (int e = lane; e < lim; e += 64) {
+                if (a.atomic_out)
+                    atomicAdd(reinterpret_cast<float*>(yg) + gbase + e, TR::to_f32(srow[e]));
+                else
+                    yg[gbase + e] = srow[e];
+            }
+        }
     }
 }
 
@@ -378,41 +533,59 @@ using KernelFn = void (*)(const PolyArgs);
 
 struct Inst {
     KernelFn fn;
-    int BM, BN, TAX, TAY, KC, lds_bytes;
+    int BM, BN, TAX, TAY, KC, threads, lds_bytes;
 };
 
-template <class TR, int MY, int MX, int TAX, int CB>
+template <class TR, int MY, int MX, int TAX, int RB, int CB, int WM, int WN, int KS>
 Inst make_inst() {
-    using C = Cfg<TR, MY, MX, TAX, 4, CB, 2, 2, 1>;
-    return Inst{&poly_kernel<TR, MY, MX, TAX, 4, CB, 2, 2, 1>, C::BM, C::BN, TAX, C::TAY, C::KC,
-                (int)(C::SMEM * C::ES)};
+    using C = Cfg<TR, MY, MX, TAX, RB, CB, WM, WN, KS>;
+    return Inst{&poly_kernel<TR, MY, MX, TAX, RB, CB, WM, WN, KS>, C::BM, C::BN, TAX, C::TAY,
+                C::KC, C::NT, (int)(C::SMEM * C::ES)};
+}
+
+// Tile shapes.  16-bit storage: 256 output rows x 128 (or 160 for five phases)
+// columns, eight waves of 64 x 64 (64 x 80) each, two per SIMD, one workgroup
+// per CU.  fp32: 128 x 128 with eight waves of 64 x 32.
+template <class TR, int MY, int MX, int CB>
+Inst inst_1d() {
+    if constexpr (sizeof(typename TR::storage) == 2)
+        return make_inst<TR, MY, MX, 256, 4, CB, 4, 2, 1>();
+    else
+        return make_inst<TR, MY, MX, 128, 4, 2, 2, 4, 1>();
+}
+
+template <class TR, int MY, int MX>
+Inst inst_2d() {
+    if constexpr (sizeof(typename TR::storage) == 2)
+        return make_inst<TR, MY, MX, 64, 4, 4, 4, 2, 1>();
+    else
+        return make_inst<TR, MY, MX, 32, 4, 2, 2, 4, 1>();
 }
 
 template <class TR>
 bool pick_inst(const Problem& p, int CB, Inst* out) {
     if (p.ndim == 1) {
-        if (CB == 5) {
+        if (CB == 5 && sizeof(typename TR::storage) == 2) {
             switch (p.mW) {
-                case 1: *out = make_inst<TR, 1, 1, 128, 5>(); return true;
-                case 2: *out = make_inst<TR, 1, 2, 128, 5>(); return true;
-                case 3: *out = make_inst<TR, 1, 3, 128, 5>(); return true;
-                case 4: *out = make_inst<TR, 1, 4, 128, 5>(); return true;
+                case 1: *out = inst_1d<TR, 1, 1, 5>(); return true;
+                case 2: *out = inst_1d<TR, 1, 2, 5>(); return true;
+                case 3: *out = inst_1d<TR, 1, 3, 5>(); return true;
+                case 4: *out = inst_1d<TR, 1, 4, 5>(); return true;
             }
             return false;
         }
         switch (p.mW) {
-            case 1: *out = make_inst<TR, 1, 1, 128, 4>(); return true;
-            case 2: *out = make_inst<TR, 1, 2, 128, 4>(); return true;
-            case 3: *out = make_inst<TR, 1, 3, 128, 4>(); return true;
-            case 4: *out = make_inst<TR, 1, 4, 128, 4>(); return true;
+            case 1: *out = inst_1d<TR, 1, 1, 4>(); return true;
+            case 2: *out = inst_1d<TR, 1, 2, 4>(); return true;
+            case 3: *out = inst_1d<TR, 1, 3, 4>(); return true;
+            case 4: *out = inst_1d<TR, 1, 4, 4>(); return true;
         }
         return false;
     }
-    if (CB != 4) return false;
-    if (p.mH == 1 && p.mW == 1) { *out = make_inst<TR, 1, 1, 32, 4>(); return true; }
-    if (p.mH == 1 && p.mW == 2) { *out = make_inst<TR, 1, 2, 32, 4>(); return true; }
-    if (p.mH == 2 && p.mW == 1) { *out = make_inst<TR, 2, 1, 32, 4>(); return true; }
-    if (p.mH == 2 && p.mW == 2) { *out = make_inst<TR, 2, 2, 32, 4>(); return true; }
+    if (p.mH == 1 && p.mW == 1) { *out = inst_2d<TR, 1, 1>(); return true; }
+    if (p.mH == 1 && p.mW == 2) { *out = inst_2d<TR, 1, 2>(); return true; }
+    if (p.mH == 2 && p.mW == 1) { *out = inst_2d<TR, 2, 1>(); return true; }
+    if (p.mH == 2 && p.mW == 2) { *out = inst_2d<TR, 2, 2>(); return true; }
     return false;
 }
 
@@ -436,7 +609,7 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
     const bool mixed_ok = !spread_y && !spread_x;  // delta_b is the same for every phase
 
     // Column tiling: TCO output channels x PT phases per tile.
-    int CB = (P % 5 == 0 && P * 16 <= 160) ? 5 : 4;
+    int CB = (p.ndim == 1 && P % 5 == 0 && P * 16 <= 160) ? 5 : 4;
     Inst in;
     if (!get_inst(p, CB, &in)) return false;
     const int64_t BN = in.BN;
@@ -469,7 +642,8 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
     const int64_t n_col_tiles = n_co_tiles * n_ph_tiles;
     const int64_t n_chunks = p.C_in_pad / in.KC;
     if (n_row_tiles * n_col_tiles > kInt32Max || P > kInt32Max / 2 || p.C_out > kInt32Max / 2 ||
-        Ax > kInt32Max / 2 || Ay > kInt32Max / 2 || n_chunks > kInt32Max)
+        Ax > kInt32Max / 2 || Ay > kInt32Max / 2 || n_chunks > kInt32Max ||
+        p.H * p.W > kInt32Max / 2 || p.Wo > kInt32Max / 2 || p.Ho > kInt32Max / 2)
         return false;
 
     a->N = p.N;
@@ -508,7 +682,9 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
     // only: partial sums meet through fp32 atomics).  Choose the split that
     // minimises (rounds of workgroups) x (chunks per workgroup).
     const int64_t tiles = n_row_tiles * n_col_tiles;
-    const int64_t per_cu = in.lds_bytes <= 80 * 1024 ? 2 : 1;
+    int64_t per_cu = (160 * 1024) / in.lds_bytes;
+    if (per_cu > 512 / in.threads) per_cu = 512 / in.threads;
+    if (per_cu < 1) per_cu = 1;
     const int64_t slots = 256 * per_cu;
     int best = 1;
     if (p.dtype == CTCONV_F32 && tiles < 2 * slots && n_chunks >= 8) {
@@ -556,7 +732,7 @@ hipError_t launch_polyphase(const Problem& p, const void* x, const void* pw, con
         if (e != hipSuccess) return e;
     }
     const int64_t tiles = a.n_row_tiles * a.n_col_tiles;
-    hipLaunchKernelGGL(in.fn, dim3((unsigned)tiles, (unsigned)splits), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(in.fn, dim3((unsigned)tiles, (unsigned)splits), dim3(in.threads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -242,3 +242,41 @@ def elu(x, out=None, stream=None):
     y = out if out is not None else torch.empty_like(x)
     ctconv_elu(x.data_ptr(), y.data_ptr(), x.numel(), dtype_code(x), _stream(stream))
     return y
+
+
+class Conv:
+    """A transposed convolution with its arguments marshalled once.
+
+    Holds the C arrays of one shape so that each call is a single foreign
+    function call (no per-call Python-side shape work).  Buffers are passed as
+    device tensors or raw pointers at call time.
+    """
+
+    def __init__(self, N: int, C_in: int, C_out: int, in_spatial, kernel, stride, padding=0,
+                 output_padding=0, dilation=1, dtype: int = CTCONV_F32,
+                 route: int = ROUTE_AUTO):
+        nd = len(in_spatial)
+        self.ndim = nd
+        self.N, self.C_in, self.C_out = int(N), int(C_in), int(C_out)
+        self.in_spatial = tuple(int(v) for v in in_spatial)
+        self.kernel = per_dim(kernel, nd)
+        self.stride = per_dim(stride, nd)
+        self.padding = per_dim(padding, nd)
+        self.output_padding = per_dim(output_padding, nd)
+        self.dilation = per_dim(dilation, nd)
+        self.dtype = dtype
+        self.route = route
+        self.out_spatial = ctconv_output_shape(self.in_spatial, self.kernel, self.stride,
+                                               self.padding, self.output_padding, self.dilation)
+        self._args = [_arr(self.in_spatial), _arr(self.kernel), _arr(self.stride),
+                      _arr(self.padding), _arr(self.output_padding), _arr(self.dilation)]
+        self._fn = load().ctconv_forward_route
+
+    def out_shape(self):
+        return (self.N, self.C_out) + self.out_spatial
+
+    def __call__(self, x_ptr: int, packed_ptr: int, bias_ptr, y_ptr: int, stream: int) -> None:
+        st = self._fn(x_ptr, packed_ptr, bias_ptr, y_ptr, self.N, self.C_in, self.C_out,
+                      self.ndim, *self._args, self.dtype, self.route, stream)
+        if st != 0:
+            raise CtconvError("ctconv_forward_route", st)
