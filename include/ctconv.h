@@ -19,6 +19,8 @@
  *    ("[XNNPACK] Lower dense transposed convs as one polyphase conv + depth to
  *    space", Summary formula).  Here it runs as an implicit GEMM on the MFMA
  *    matrix cores with the interleave, slice and bias fused into its epilogue.
+ *    Its kernels cover m <= 4 (1-D) or m <= 2 per dimension (2-D) and input
+ *    rows of at least 8 bytes (W >= 4 for bf16/fp16, W >= 2 for fp32).
  *  - gather: every other shape, one output at a time from the tap condition.
  *
  * Layouts.  x [N, C_in, L] or [N, C_in, H, W]; y [N, C_out, L_out] or

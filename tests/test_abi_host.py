@@ -172,3 +172,14 @@ def test_routes_of_workloads(lib, name, route):
 def test_route_rule(lib, k, s, p, op, d, route):
     # polyphase iff k % s == 0, d == 1, op == 0 (and m = k/s within the compiled taps)
     assert C.ctconv_query_route(2, 16, 16, (50,), k, s, p, op, d, 1) == route
+
+
+@pytest.mark.parametrize("sp,dt,route", [
+    ((1,), 0, 2), ((2,), 0, 1), ((3,), 1, 2), ((4,), 1, 1), ((3,), 2, 2),
+    ((9, 3), 1, 2), ((9, 4), 1, 1), ((1, 2), 0, 1),
+])
+def test_route_short_rows(lib, sp, dt, route):
+    # the polyphase kernel loads 8 bytes of an input row at a time: rows
+    # shorter than that go to the gather kernel
+    k, s, p = ((8,), (4,), (2,)) if len(sp) == 1 else ((4, 4), (2, 2), (1, 1))
+    assert C.ctconv_query_route(2, 16, 16, sp, k, s, p, 0, 1, dt) == route

@@ -122,6 +122,10 @@ FULL_CASES = [
     ("asym2d", "f32", 2, 36, 20, (17, 45), (2, 6), (1, 3), (0, 2), (0, 0), (1, 1), True),
     ("asym2d_m1", "bf16", 1, 64, 48, (33, 18), (2, 4), (2, 2), (0, 1), (0, 0), (1, 1), False),
     ("len1", "f32", 3, 40, 16, (1,), (8,), (4,), (2,), (0,), (1,), True),
+    # shortest rows the polyphase kernel takes (one 8-byte load per row)
+    ("len2_f32", "f32", 3, 40, 16, (2,), (8,), (4,), (2,), (0,), (1,), True),
+    ("len4_bf16", "bf16", 3, 40, 24, (4,), (8,), (4,), (3,), (0,), (1,), True),
+    ("w4_2d_bf16", "bf16", 2, 32, 16, (5, 4), (4, 4), (2, 2), (1, 1), (0, 0), (1, 1), True),
 ]
 
 

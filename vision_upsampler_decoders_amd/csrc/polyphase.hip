@@ -93,6 +93,13 @@ struct Mma<TF32> {
     }
 };
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_u __attribute__((ext_vector_type(2), aligned(1)));
+
+__device__ inline u32x2 load8_unaligned(const void* p) {
+    return *reinterpret_cast<const u32x2_u*>(p);
+}
+
 __device__ inline u32x4 load16_unaligned(const void* p) {
     return *reinterpret_cast<const u32x4_u*>(p);
 }
@@ -101,36 +108,11 @@ __device__ inline void store16_unaligned(void* p, const u32x4 v) {
     *reinterpret_cast<u32x4_u*>(p) = v;
 }
 
-// VEC elements of one row at clamped positions p0 .. p0+VEC-1 (edge tiles).
-template <typename S>
-__device__ inline u32x4 load_row_clamped(const S* rowp, int p0, int W) {
-    if constexpr (sizeof(S) == 2) {
-        u16x8 v;
+// 8 channels x 4 positions of 16-bit elements -> 4 rows of 8 channels
+// (v_perm_b32 gathers one half-word from each of two channels per dword).
+__device__ inline void transpose_block(const u32x2 (&in)[8], u32x4 (&out)[4]) {
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            int pos = p0 + p;
-            pos = pos < 0 ? 0 : (pos >= W ? W - 1 : pos);
-            v[p] = rowp[pos];
-        }
-        return __builtin_bit_cast(u32x4, v);
-    } else {
-        u32x4 v;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            int pos = p0 + p;
-            pos = pos < 0 ? 0 : (pos >= W ? W - 1 : pos);
-            v[p] = __builtin_bit_cast(uint32_t, rowp[pos]);
-        }
-        return __builtin_bit_cast(u32x4, v);
-    }
-}
-
-// 8x8 transpose of 16-bit elements held as eight 16-byte rows: out[p] holds
-// element p of in[0..7] (v_perm_b32 gathers one half-word from each of two
-// rows per output dword).
-__device__ inline void transpose8x16(const u32x4 (&in)[8], u32x4 (&out)[8]) {
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
+    for (int p = 0; p < 4; ++p) {
         const unsigned sel = (p & 1) ? 0x07060302u : 0x05040100u;
         u32x4 d;
 #pragma unroll
@@ -140,10 +122,10 @@ __device__ inline void transpose8x16(const u32x4 (&in)[8], u32x4 (&out)[8]) {
     }
 }
 
-// 4x4 transpose of 32-bit elements (register renaming only).
-__device__ inline void transpose4x32(const u32x4 (&in)[4], u32x4 (&out)[4]) {
+// 4 channels x 2 positions of 32-bit elements -> 2 rows of 4 channels.
+__device__ inline void transpose_block(const u32x2 (&in)[4], u32x4 (&out)[2]) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) out[p] = u32x4{in[0][p], in[1][p], in[2][p], in[3][p]};
+    for (int p = 0; p < 2; ++p) out[p] = u32x4{in[0][p], in[1][p], in[2][p], in[3][p]};
 }
 
 template <class TR, int MY, int MX, int TAX, int RB, int CB, int WM, int WN, int KS>
@@ -164,10 +146,11 @@ struct Cfg {
     static constexpr int BROWS = T * BN;
     static constexpr int STAGE = (XROWS + BROWS) * RSA;
     static constexpr int NG = KC / VEC;                           // channel groups per chunk
+    static constexpr int NP = 8 / ES;                             // positions per load item
     static constexpr int NW = WM * WN;                            // waves per workgroup
     static constexpr int NT = 64 * NW;                            // threads per workgroup
     // load items are split into NW contiguous per-wave ranges (coalesced lanes)
-    static constexpr int XMAX = WYM * (WXP / VEC) * NG;
+    static constexpr int XMAX = WYM * (WXP / NP) * NG;
     static constexpr int XITEMS = ((XMAX + NW - 1) / NW + 63) / 64;
     static constexpr int BMAX = BROWS * NG;
     static constexpr int BITEMS = ((BMAX + NW - 1) / NW + 63) / 64;
@@ -212,53 +195,87 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
     const int wm = wave / WN, wn = wave % WN;
     const int li = lane & 15, lg = lane >> 4;
 
-    // ---- x staging descriptors: item = (window row, VEC positions, VEC channels)
+    // ---- x staging descriptors: item = (window row, NP positions, VEC channels)
+    // Each channel of an item is one 8-byte global load (NP positions); the
+    // VEC x NP block is transposed in registers into NP LDS rows of VEC
+    // channels.  Channel group fastest across lanes: the LDS rows written by
+    // one store instruction are NP apart, which maps 16 lanes onto 16 distinct
+    // 16-byte bank groups, and the lanes sharing a channel group still read a
+    // run that is contiguous along the spatial axis.
+    constexpr int NP = C::NP;
     const int64_t HW = a.H * a.W;
-    const int ngx = WXP / VEC;
+    const int ngx = WXP / NP;
     const int xitems = a.WY * ngx * NG;
     const int xper = (xitems + C::NW - 1) / C::NW;  // items per wave
-    int xrow[C::XITEMS];   // element offset of (row iy, position P0) within a channel plane
-    int xp0[C::XITEMS];    // first position P0 (may be negative)
-    int xg0[C::XITEMS];    // channel offset of the group within a chunk
-    int xlds[C::XITEMS];   // LDS element offset of the first position row (-1: no item)
-    bool xrowok[C::XITEMS];
+    // Per item: byte offset (within the image) of channel 0 of the group at
+    // the clamped in-row start position, the realignment shift (positions),
+    // the valid-position mask, the group's channel offset and its LDS slot.
+    uint32_t xgoff[C::XITEMS];  // channel-group offset (bytes) within a chunk
+    uint32_t xroff[C::XITEMS];  // row/position offset (bytes) within a channel plane
+    int xsh[C::XITEMS];
+    uint32_t xpm[C::XITEMS];
+    int xg0[C::XITEMS];
+    // LDS element offset of the first position row.  Lanes without an item
+    // get the 16-byte padding at the end of NP rows (never read by the
+    // MFMA operand loads), spread over rows, so that every store is
+    // unconditional.
+    int xlds[C::XITEMS];
 #pragma unroll
     for (int it = 0; it < C::XITEMS; ++it) {
         const int qw = lane + 64 * it;
         const int q = wave * xper + qw;
-        xlds[it] = -1;
-        xrow[it] = 0;
-        xp0[it] = 0;
+        xlds[it] = (lane % (C::XROWS / NP)) * NP * RSA + KC;
+        xgoff[it] = 0;
+        xroff[it] = 0;
+        xsh[it] = 0;
+        xpm[it] = 0;
         xg0[it] = 0;
-        xrowok[it] = false;
         if (qw < xper && q < xitems) {
-            // channel group fastest: lanes g = 0..NG-1 of one position group write
-            // adjacent 16-byte slots of the same LDS rows (at most 2-way bank
-            // conflicts), while the lanes sharing a g still read 16-byte runs
-            // that are contiguous along the spatial axis
             const int g = q % NG;
             const int r2 = q / NG;
             const int gx = r2 % ngx;
             const int wy = r2 / ngx;
             const int iy = wy0 + wy;
-            xrowok[it] = iy >= 0 && iy < a.H;
-            xp0[it] = wx0 + gx * VEC;
-            xrow[it] = (xrowok[it] ? iy : 0) * (int)a.W;
+            const bool rowok = iy >= 0 && iy < a.H;
+            const int p0 = wx0 + gx * NP;
+            // one NP-element load from an in-row start (the planner admits
+            // only rows of at least NP elements, so one always exists)
+            int p0c = p0 < 0 ? 0 : p0;
+            if (p0c > (int)a.W - NP) p0c = (int)a.W - NP;
+            if (p0c < 0) p0c = 0;
+            uint32_t pm = 0;
+#pragma unroll
+            for (int p = 0; p < NP; ++p)
+                pm |= (rowok && p0 + p >= 0 && p0 + p < a.W) ? (1u << p) : 0u;
+            xpm[it] = pm;
+            // data for position p sits at loaded index p + shift; an item with
+            // no valid position is masked entirely, so its shift is irrelevant
+            const int shft = p0 - p0c;
+            xsh[it] = (shft > -NP && shft < NP) ? shft : 0;
+            xgoff[it] = (uint32_t)((int64_t)g * VEC * HW * C::ES);
+            xroff[it] = (uint32_t)(((int64_t)(rowok ? iy : 0) * a.W + p0c) * C::ES);
             xg0[it] = g * VEC;
-            xlds[it] = (wy * WXP + gx * VEC) * RSA + g * VEC;
+            xlds[it] = (wy * WXP + gx * NP) * RSA + g * VEC;
         }
     }
-    const S* xn = xg + n * a.C_in * HW;
+    const char* xn = reinterpret_cast<const char*>(xg + n * a.C_in * HW);
+    const uint32_t ch_bytes = (uint32_t)(HW * C::ES);  // one channel plane
 
-    int64_t boff[C::BITEMS];  // packed-weight element offset, -1 for a zero row
+    // B items: packed-weight element offset (0 for a zero row: the load is
+    // made anyway and its value dropped at LDS store time, so that no load
+    // sits under a branch) and LDS slot (row padding for lanes without one).
+    int64_t boff[C::BITEMS];
+    bool bval[C::BITEMS];
+    const char* pwb = reinterpret_cast<const char*>(pwg);
     int blds[C::BITEMS];
     constexpr int bper = (C::BMAX + C::NW - 1) / C::NW;
 #pragma unroll
     for (int it = 0; it < C::BITEMS; ++it) {
         const int qw = lane + 64 * it;
         const int q = wave * bper + qw;
-        boff[it] = -1;
-        blds[it] = -1;
+        boff[it] = 0;
+        bval[it] = false;
+        blds[it] = (lane % C::BROWS) * RSA + KC;  // row padding: no item
         if (qw < bper && q < C::BMAX) {
             const int row = q / NG, piece = q % NG;
             const int r = row / BN, tc = row % BN;
@@ -267,6 +284,7 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
                 const int by = b / a.sx, bx = b % a.sx;
                 const int j = ((by + a.py) % a.sy) * a.sx + (bx + a.px) % a.sx;
                 boff[it] = (((int64_t)j * a.C_out + co) * T + r) * a.C_in_pad + piece * VEC;
+                bval[it] = true;
             }
             blds[it] = (r * BN + tc) * RSA + piece * VEC;
         }
@@ -288,80 +306,78 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
         ddx[cb] = __builtin_amdgcn_readfirstlane(dx);
     }
 
-    u32x4 xr[C::XITEMS][VEC];
-    uint32_t xmask[C::XITEMS];  // bit p: position p valid; bit 8+e: channel e valid
-    u32x4 br[C::BITEMS];
+    // Two register buffers: the loads of chunk c+2 are issued before the
+    // MFMAs of chunk c and stored to LDS after those of chunk c+1.
+    using XBuf = u32x2[C::XITEMS][VEC];
+    using XMask = uint32_t[C::XITEMS];  // bit p: position p valid; bit 8+e: channel e valid
+    using BBuf = u32x4[C::BITEMS];
+    XBuf xr0, xr1;
+    XMask xm0, xm1;
+    BBuf br0, br1;
 
     // Global -> registers.  Loads only: nothing here consumes a loaded value,
-    // so the loads of chunk c+1 stay in flight while chunk c is computed.
-    auto gload = [&](int c) __attribute__((always_inline)) {
+    // so no wait is needed before the MFMAs of the current chunk.  Channels
+    // past C_in (ragged last chunk) load channel 0 of the group and are
+    // zeroed at LDS store time, as are positions outside the row.
+    auto gload = [&](int c, XBuf& xr, XMask& xm, BBuf& br) __attribute__((always_inline)) {
         const int cbase = c * KC;
+        const uint32_t cbytes = (uint32_t)cbase * ch_bytes;
+        const bool cfull = cbase + KC <= a.C_in;
 #pragma unroll
         for (int it = 0; it < C::XITEMS; ++it) {
-            xmask[it] = 0;
-            if (xlds[it] < 0) continue;
-            const int p0 = xp0[it];
-            const bool inside = p0 >= 0 && p0 + VEC <= a.W;
-            uint32_t m = 0;
+            // lanes without an item load channel 0 of row 0 (offsets 0) and
+            // skip the LDS store
+            uint32_t m = xpm[it];
+            if (cfull) {
+                m |= ((1u << VEC) - 1u) << 8;
+            } else {
 #pragma unroll
-            for (int p = 0; p < VEC; ++p)
-                m |= (xrowok[it] && p0 + p >= 0 && p0 + p < a.W) ? (1u << p) : 0u;
-            const int ch0 = cbase + xg0[it];
-            const S* base = xn + (int64_t)ch0 * HW + xrow[it];
+                for (int e = 0; e < VEC; ++e) m |= (cbase + xg0[it] + e < a.C_in) ? (1u << (8 + e)) : 0u;
+            }
+            xm[it] = m;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
-                const bool chok = ch0 + e < a.C_in;
-                m |= chok ? (1u << (8 + e)) : 0u;
-                const S* rowp = chok ? base + (int64_t)e * HW : xn + xrow[it];
-                // clamped in-row addresses at the edges; masked at LDS store time
-                xr[it][e] = inside ? load16_unaligned(rowp + p0)
-                                   : load_row_clamped(rowp, p0, (int)a.W);
-            }
-            xmask[it] = m;
-        }
-#pragma unroll
-        for (int it = 0; it < C::BITEMS; ++it) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (boff[it] >= 0) v = *reinterpret_cast<const u32x4*>(pwg + boff[it] + cbase);
-            br[it] = v;
-        }
-    };
-
-    auto lstore = [&](int st) __attribute__((always_inline)) {
-        S* xs = smem + st * C::STAGE;
-        S* bs = xs + C::XROWS * RSA;
-        const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int it = 0; it < C::XITEMS; ++it) {
-            if (xlds[it] < 0) continue;
-            const uint32_t m = xmask[it];
-            constexpr uint32_t kAll = (1u << (8 + VEC)) - (1u << 8) + (1u << VEC) - 1u;
-            u32x4 in[VEC], tr[VEC];
-            if (m == kAll) {  // every position and channel valid: no masking
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) in[e] = xr[it][e];
-            } else {
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) in[e] = (m & (1u << (8 + e))) ? xr[it][e] : z;
-            }
-            if constexpr (VEC == 8)
-                transpose8x16(in, tr);
-            else
-                transpose4x32(in, tr);
-            if (m == kAll) {
-#pragma unroll
-                for (int p = 0; p < VEC; ++p)
-                    *reinterpret_cast<u32x4*>(xs + xlds[it] + p * RSA) = tr[p];
-            } else {
-#pragma unroll
-                for (int p = 0; p < VEC; ++p)
-                    *reinterpret_cast<u32x4*>(xs + xlds[it] + p * RSA) =
-                        (m & (1u << p)) ? tr[p] : z;
+                // channels past C_in read channel 0 of the image (always
+                // present) and are zeroed at store time
+                const uint32_t off = (m & (1u << (8 + e)))
+                                         ? cbytes + xgoff[it] + e * ch_bytes + xroff[it]
+                                         : xroff[it];
+                xr[it][e] = load8_unaligned(xn + off);
             }
         }
 #pragma unroll
         for (int it = 0; it < C::BITEMS; ++it)
-            if (blds[it] >= 0) *reinterpret_cast<u32x4*>(bs + blds[it]) = br[it];
+            br[it] = *reinterpret_cast<const u32x4*>(pwb + (boff[it] + cbase) * C::ES);
+    };
+
+    auto lstore = [&](int st, const XBuf& xr, const XMask& xm, const BBuf& br)
+                      __attribute__((always_inline)) {
+        S* xs = smem + st * C::STAGE;
+        S* bs = xs + C::XROWS * RSA;
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        const u32x2 z2 = {0u, 0u};
+        // Branch-free: every lane realigns (shift 0 away from row edges),
+        // masks and stores, so no wait for the loads sits under a branch.
+#pragma unroll
+        for (int it = 0; it < C::XITEMS; ++it) {
+            const uint32_t m = xm[it];
+            const int sh = xsh[it] * (int)(8 * C::ES);
+            u32x2 in[VEC];
+            u32x4 tr[NP];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                uint64_t v = __builtin_bit_cast(uint64_t, xr[it][e]);
+                v = sh >= 0 ? (v >> sh) : (v << -sh);
+                in[e] = (m & (1u << (8 + e))) ? __builtin_bit_cast(u32x2, v) : z2;
+            }
+            transpose_block(in, tr);
+#pragma unroll
+            for (int p = 0; p < NP; ++p)
+                *reinterpret_cast<u32x4*>(xs + xlds[it] + p * RSA) = (m & (1u << p)) ? tr[p] : z;
+        }
+#pragma unroll
+        for (int it = 0; it < C::BITEMS; ++it)
+            *reinterpret_cast<u32x4*>(bs + blds[it]) = bval[it] ? br[it] : z;
     };
 
     f32x4 acc[RB][CB];
@@ -381,11 +397,12 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
 
     // Shift bookkeeping: column block cb belongs to class (dd_y, dd_x) with
     // dd in {0, 1} per dimension; for tap (ry, rx) its A rows sit at window
-    // offset (dd_y + MY-1-ry, dd_x + MX-1-rx).  Per tap, the B fragments of all
-    // column blocks are loaded, then for every class present in this wave the
-    // A fragments at that class's offset, then the MFMAs of the class's
-    // column blocks.  Classes and their presence mask are wave-uniform.
+    // offset (dd_y + MY-1-ry, dd_x + MX-1-rx).  Classes and their presence
+    // mask are wave-uniform.  Per k-step: B fragments of every tap (loaded
+    // once when they fit in registers), then for each class present the A
+    // fragments of all taps, then that class's MFMAs.
     constexpr bool Y2 = C::TAY > 1;  // 2-D tile: the row offset may differ too
+    constexpr bool BPRE = CB * T <= 8;
     int cls[CB];
     uint32_t clsmask = 0;
 #pragma unroll
@@ -399,53 +416,92 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int kofs = ks * C::KSTEP + lg * VEC;
+            u32x4 bpre[BPRE ? CB : 1][BPRE ? T : 1];
+            if constexpr (BPRE) {
 #pragma unroll
-            for (int ry = 0; ry < MY; ++ry)
+                for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-                for (int rx = 0; rx < MX; ++rx) {
-                    const int r = ry * MX + rx;
+                    for (int r = 0; r < T; ++r)
+                        bpre[cb][r] = *reinterpret_cast<const u32x4*>(
+                            bs + (r * BN + bcol + cb * 16) * RSA + kofs);
+            }
+#pragma unroll
+            for (int c = 0; c < (Y2 ? 4 : 2); ++c) {
+                if (!(clsmask & (1u << c))) continue;
+                // one tap at a time: its RB A fragments, its CB B fragments,
+                // then the MFMAs of the column blocks in this class
+#pragma unroll
+                for (int r = 0; r < T; ++r) {
+                    const int ey = (c >> 1) + MY - 1 - r / MX;
+                    const int ex = (c & 1) + MX - 1 - r % MX;
+                    u32x4 afr[RB];
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        afr[rb] = *reinterpret_cast<const u32x4*>(
+                            xs + (arow[rb] + ey * WXP + ex) * RSA + kofs);
                     u32x4 bfr[CB];
 #pragma unroll
-                    for (int cb = 0; cb < CB; ++cb)
-                        bfr[cb] = *reinterpret_cast<const u32x4*>(
-                            bs + (r * BN + bcol + cb * 16) * RSA + kofs);
-#pragma unroll
-                    for (int c = 0; c < (Y2 ? 4 : 2); ++c) {
-                        if (!(clsmask & (1u << c))) continue;
-                        const int ey = (c >> 1) + MY - 1 - ry;
-                        const int ex = (c & 1) + MX - 1 - rx;
-                        u32x4 afr[RB];
-#pragma unroll
-                        for (int rb = 0; rb < RB; ++rb)
-                            afr[rb] = *reinterpret_cast<const u32x4*>(
-                                xs + (arow[rb] + ey * WXP + ex) * RSA + kofs);
-#pragma unroll
-                        for (int cb = 0; cb < CB; ++cb)
-                            if (cls[cb] == c) {
-#pragma unroll
-                                for (int rb = 0; rb < RB; ++rb)
-                                    Mma<TR>::step(acc[rb][cb], afr[rb], bfr[cb]);
-                            }
+                    for (int cb = 0; cb < CB; ++cb) {
+                        if constexpr (BPRE)
+                            bfr[cb] = bpre[cb][r];
+                        else
+                            bfr[cb] = *reinterpret_cast<const u32x4*>(
+                                bs + (r * BN + bcol + cb * 16) * RSA + kofs);
                     }
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+                        if (cls[cb] == c) {
+#pragma unroll
+                            for (int rb = 0; rb < RB; ++rb)
+                                Mma<TR>::step(acc[rb][cb], afr[rb], bfr[cb]);
+                        }
                 }
+            }
         }
     };
 
-    // ---- main loop over input-channel chunks -------------------------------
+    // ---- main loop over input-channel chunks (two chunks per iteration) ----
     const int c_begin = blockIdx.y * a.chunks_per_split;
     const int c_end = min(c_begin + a.chunks_per_split, a.n_chunks);
-    if (c_begin < c_end) {
-        gload(c_begin);
-        lstore(0);
+    const int nck = c_end - c_begin;
+    if (nck > 0) {
+        // Prefetches are issued unconditionally (past the last chunk they
+        // re-read it and the values are never stored): a conditional load
+        // would make each buffer a merge of old and new registers, which the
+        // compiler resolves with copies that wait for the loads in flight.
+        const int c_last = c_end - 1;
+        gload(c_begin, xr0, xm0, br0);
+        gload(min(c_begin + 1, c_last), xr1, xm1, br1);
+        lstore(0, xr0, xm0, br0);
         __syncthreads();
-        for (int c = c_begin; c < c_end; ++c) {
-            const int st = (c - c_begin) & 1;
-            if (c + 1 < c_end) gload(c + 1);
-            compute(st);
-            if (c + 1 < c_end) lstore(st ^ 1);
+        // Steady state: chunks i and i+1 with at least one more chunk after
+        // them, so every store below is unconditional (a skipped store
+        // would leave its loads "in flight" for the compiler at the loop
+        // head, where it then waits for every load).
+        int i = 0;
+        for (; i + 2 < nck; i += 2) {
+            // chunk i in stage 0; buffer 0 is free, buffer 1 holds chunk i+1
+            gload(c_begin + i + 2, xr0, xm0, br0);
+            compute(0);
+            lstore(1, xr1, xm1, br1);
+            __syncthreads();
+            // chunk i+1 in stage 1; buffer 1 is free, buffer 0 holds chunk i+2
+            gload(min(c_begin + i + 3, c_last), xr1, xm1, br1);
+            compute(1);
+            lstore(0, xr0, xm0, br0);
             __syncthreads();
         }
+        // last one or two chunks: chunk i in stage 0, chunk i+1 in buffer 1
+        compute(0);
+        if (i + 1 < nck) {
+            lstore(1, xr1, xm1, br1);
+            __syncthreads();
+            compute(1);
+        }
     }
+    // the output staging below reuses the operand stages: every wave must be
+    // done reading them
+    __syncthreads();
 
     // ---- epilogue: bias, round, stage in output order, store ---------------
     const S* __restrict__ biasg = static_cast<const S*>(a.bias);
@@ -546,20 +602,31 @@ Inst make_inst() {
 // Tile shapes.  16-bit storage: 256 output rows x 128 (or 160 for five phases)
 // columns, eight waves of 64 x 64 (64 x 80) each, two per SIMD, one workgroup
 // per CU.  fp32: 128 x 128 with eight waves of 64 x 32.
+#ifndef CTCONV_TILE_VARIANT
+#define CTCONV_TILE_VARIANT 2
+#endif
 template <class TR, int MY, int MX, int CB>
 Inst inst_1d() {
-    if constexpr (sizeof(typename TR::storage) == 2)
-        return make_inst<TR, MY, MX, 256, 4, CB, 4, 2, 1>();
-    else
+    if constexpr (sizeof(typename TR::storage) == 2) {
+        if constexpr (CTCONV_TILE_VARIANT == 1)
+            return make_inst<TR, MY, MX, 128, 4, CB, 2, 2, 1>();
+        else
+            return make_inst<TR, MY, MX, 256, 4, CB, 4, 2, 1>();
+    } else {
         return make_inst<TR, MY, MX, 128, 4, 2, 2, 4, 1>();
+    }
 }
 
 template <class TR, int MY, int MX>
 Inst inst_2d() {
-    if constexpr (sizeof(typename TR::storage) == 2)
-        return make_inst<TR, MY, MX, 64, 4, 4, 4, 2, 1>();
-    else
+    if constexpr (sizeof(typename TR::storage) == 2) {
+        if constexpr (CTCONV_TILE_VARIANT == 1)
+            return make_inst<TR, MY, MX, 32, 4, 4, 2, 2, 1>();
+        else
+            return make_inst<TR, MY, MX, 64, 4, 4, 4, 2, 1>();
+    } else {
         return make_inst<TR, MY, MX, 32, 4, 2, 2, 4, 1>();
+    }
 }
 
 template <class TR>
@@ -604,6 +671,8 @@ constexpr int64_t kInt32Max = 2147483647;
 bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
     if (p.kH % p.sH || p.kW % p.sW || p.dH != 1 || p.dW != 1 || p.opH || p.opW) return false;
     if (p.H == 0 || p.W == 0 || p.N == 0) return false;
+    // every staged x load covers 8 bytes of one input row
+    if (p.W * (p.dtype == CTCONV_F32 ? 4 : 2) < 8) return false;
     const int64_t P = p.P;
     const bool spread_y = (p.pH % p.sH) != 0, spread_x = (p.pW % p.sW) != 0;
     const bool mixed_ok = !spread_y && !spread_x;  // delta_b is the same for every phase
@@ -645,6 +714,8 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
         Ax > kInt32Max / 2 || Ay > kInt32Max / 2 || n_chunks > kInt32Max ||
         p.H * p.W > kInt32Max / 2 || p.Wo > kInt32Max / 2 || p.Ho > kInt32Max / 2)
         return false;
+    // x staging uses 32-bit byte offsets within one image
+    if (p.C_in_pad * p.H * p.W * (p.dtype == CTCONV_F32 ? 4 : 2) > (int64_t)4000000000LL) return false;
 
     a->N = p.N;
     a->C_in = p.C_in;
