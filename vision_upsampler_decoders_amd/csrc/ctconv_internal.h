@@ -77,6 +77,9 @@ struct PolyArgs {
     int dminy, dminx;      // floor(p / s)
     int spready, spreadx;  // 1 when floor((b + p) / s) differs between phases
     int WY, WX;            // x window per tile (rows x columns)
+    int xofs;              // window start moved back by this many positions so
+                           // that every x load is 8-byte aligned (0 when rows
+                           // are not a multiple of 8 bytes)
     int TCO, PT;           // output channels and phases per column tile
     int phase_subset;      // 0: a column tile holds every phase; 1: a run of PT phases
     int n_ph_tiles, n_col_tiles;

@@ -141,12 +141,14 @@ struct Cfg {
     static constexpr int TAY = BM / TAX;
     static constexpr int T = MY * MX;
     static constexpr int WYM = TAY + MY - 1 + (TAY > 1 ? 1 : 0);  // window rows (max)
-    static constexpr int WXP = (TAX + MX + VEC - 1) / VEC * VEC;  // window columns, padded
+    static constexpr int NP = 8 / ES;                             // positions per load item
+    // window columns: the tile, the halo, the shift class and up to NP-1
+    // positions of alignment shift, padded to whole fragments
+    static constexpr int WXP = (TAX + MX + NP - 1 + VEC - 1) / VEC * VEC;
     static constexpr int XROWS = WYM * WXP;
     static constexpr int BROWS = T * BN;
     static constexpr int STAGE = (XROWS + BROWS) * RSA;
     static constexpr int NG = KC / VEC;                           // channel groups per chunk
-    static constexpr int NP = 8 / ES;                             // positions per load item
     static constexpr int NW = WM * WN;                            // waves per workgroup
     static constexpr int NT = 64 * NW;                            // threads per workgroup
     // load items are split into NW contiguous per-wave ranges (coalesced lanes)
@@ -156,6 +158,10 @@ struct Cfg {
     static constexpr int BITEMS = ((BMAX + NW - 1) / NW + 63) / 64;
     static constexpr int EPI = BM * BN + BN * VEC;  // staged output tile, padded
     static constexpr int SMEM = (2 * STAGE > EPI ? 2 * STAGE : EPI);
+    // global -> register prefetch depth in chunks: one wave per SIMD with a
+    // 128 x 128-class wave tile has long MFMA phases but no registers for a
+    // second buffer
+    static constexpr int PF = ((NW == 4 && RB * CB >= 32) || KS >= 2) ? 1 : 2;
     static_assert(BM % TAX == 0 && TAX % 16 == 0, "tile rows");
     static_assert(NW == 4 || NW == 8, "four or eight waves");
     static_assert(SMEM * ES <= 160 * 1024, "LDS");
@@ -189,7 +195,7 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
     const int b0 = (col_tile % a.n_ph_tiles) * a.PT;
     const int ay0 = ty_t * C::TAY, ax0 = tx_t * TAX;
     const int wy0 = ay0 + a.dminy - (MY - 1);
-    const int wx0 = ax0 + a.dminx - (MX - 1);
+    const int wx0 = ax0 + a.dminx - (MX - 1) - a.xofs;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
@@ -210,6 +216,7 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
     // Per item: byte offset (within the image) of channel 0 of the group at
     // the clamped in-row start position, the realignment shift (positions),
     // the valid-position mask, the group's channel offset and its LDS slot.
+    uint32_t xlo[C::XITEMS];    // xgoff + xroff: the lane's offset for a full chunk
     uint32_t xgoff[C::XITEMS];  // channel-group offset (bytes) within a chunk
     uint32_t xroff[C::XITEMS];  // row/position offset (bytes) within a channel plane
     int xsh[C::XITEMS];
@@ -257,15 +264,26 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
             xg0[it] = g * VEC;
             xlds[it] = (wy * WXP + gx * NP) * RSA + g * VEC;
         }
+        xlo[it] = xgoff[it] + xroff[it];
     }
+    // The whole wave's items sit inside their rows with no realignment shift
+    // (true for most tiles): its LDS stores need no shift and no masks.  Lanes
+    // without an item count as inside (they write row padding).
+    bool inside = true;
+#pragma unroll
+    for (int it = 0; it < C::XITEMS; ++it) {
+        const bool item = (wave * xper + lane + 64 * it < xitems) && (lane + 64 * it < xper);
+        inside = inside && (!item || (xpm[it] == (1u << NP) - 1u && xsh[it] == 0));
+    }
+    const bool wave_inside = __all(inside);
     const char* xn = reinterpret_cast<const char*>(xg + n * a.C_in * HW);
     const uint32_t ch_bytes = (uint32_t)(HW * C::ES);  // one channel plane
 
-    // B items: packed-weight element offset (0 for a zero row: the load is
-    // made anyway and its value dropped at LDS store time, so that no load
-    // sits under a branch) and LDS slot (row padding for lanes without one).
+    // B items: packed-weight element offset (0 for a row past C_out or past
+    // the phases: the load is made anyway so that no load sits under a
+    // branch; such rows feed only columns that are never stored) and LDS slot
+    // (row padding for lanes without one).
     int64_t boff[C::BITEMS];
-    bool bval[C::BITEMS];
     const char* pwb = reinterpret_cast<const char*>(pwg);
     int blds[C::BITEMS];
     constexpr int bper = (C::BMAX + C::NW - 1) / C::NW;
@@ -274,7 +292,6 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
         const int qw = lane + 64 * it;
         const int q = wave * bper + qw;
         boff[it] = 0;
-        bval[it] = false;
         blds[it] = (lane % C::BROWS) * RSA + KC;  // row padding: no item
         if (qw < bper && q < C::BMAX) {
             const int row = q / NG, piece = q % NG;
@@ -284,7 +301,6 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
                 const int by = b / a.sx, bx = b % a.sx;
                 const int j = ((by + a.py) % a.sy) * a.sx + (bx + a.px) % a.sx;
                 boff[it] = (((int64_t)j * a.C_out + co) * T + r) * a.C_in_pad + piece * VEC;
-                bval[it] = true;
             }
             blds[it] = (r * BN + tc) * RSA + piece * VEC;
         }
@@ -313,36 +329,49 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
     using BBuf = u32x4[C::BITEMS];
     XBuf xr0, xr1;
     XMask xm0, xm1;
+    bool xf0 = true, xf1 = true;  // buffer holds a full chunk (wave-uniform)
     BBuf br0, br1;
 
     // Global -> registers.  Loads only: nothing here consumes a loaded value,
     // so no wait is needed before the MFMAs of the current chunk.  Channels
     // past C_in (ragged last chunk) load channel 0 of the group and are
     // zeroed at LDS store time, as are positions outside the row.
-    auto gload = [&](int c, XBuf& xr, XMask& xm, BBuf& br) __attribute__((always_inline)) {
+    auto gload = [&](int c, XBuf& xr, XMask& xm, BBuf& br, bool& full)
+                     __attribute__((always_inline)) {
         const int cbase = c * KC;
         const uint32_t cbytes = (uint32_t)cbase * ch_bytes;
         const bool cfull = cbase + KC <= a.C_in;
+        full = cfull;
+        if (cfull) {
+            // every channel present: a wave-uniform base per channel plus the
+            // lane's offset (no per-lane address arithmetic)
+            const char* xc = xn + cbytes;
 #pragma unroll
-        for (int it = 0; it < C::XITEMS; ++it) {
-            // lanes without an item load channel 0 of row 0 (offsets 0) and
-            // skip the LDS store
-            uint32_t m = xpm[it];
-            if (cfull) {
-                m |= ((1u << VEC) - 1u) << 8;
-            } else {
+            for (int it = 0; it < C::XITEMS; ++it) {
+                xm[it] = xpm[it] | (((1u << VEC) - 1u) << 8);
 #pragma unroll
-                for (int e = 0; e < VEC; ++e) m |= (cbase + xg0[it] + e < a.C_in) ? (1u << (8 + e)) : 0u;
+                for (int e = 0; e < VEC; ++e)
+                    xr[it][e] = load8_unaligned(xc + (size_t)e * ch_bytes + xlo[it]);
             }
-            xm[it] = m;
+        } else {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                // channels past C_in read channel 0 of the image (always
-                // present) and are zeroed at store time
-                const uint32_t off = (m & (1u << (8 + e)))
-                                         ? cbytes + xgoff[it] + e * ch_bytes + xroff[it]
-                                         : xroff[it];
-                xr[it][e] = load8_unaligned(xn + off);
+            for (int it = 0; it < C::XITEMS; ++it) {
+                // lanes without an item load channel 0 of row 0 (offsets 0)
+                // and write row padding
+                uint32_t m = xpm[it];
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    m |= (cbase + xg0[it] + e < a.C_in) ? (1u << (8 + e)) : 0u;
+                xm[it] = m;
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) {
+                    // channels past C_in read channel 0 of the image (always
+                    // present) and are zeroed at store time
+                    const uint32_t off = (m & (1u << (8 + e)))
+                                             ? cbytes + xgoff[it] + e * ch_bytes + xroff[it]
+                                             : xroff[it];
+                    xr[it][e] = load8_unaligned(xn + off);
+                }
             }
         }
 #pragma unroll
@@ -350,14 +379,25 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
             br[it] = *reinterpret_cast<const u32x4*>(pwb + (boff[it] + cbase) * C::ES);
     };
 
-    auto lstore = [&](int st, const XBuf& xr, const XMask& xm, const BBuf& br)
+    auto lstore = [&](int st, const XBuf& xr, const XMask& xm, const BBuf& br, const bool full)
                       __attribute__((always_inline)) {
         S* xs = smem + st * C::STAGE;
         S* bs = xs + C::XROWS * RSA;
         const u32x4 z = {0u, 0u, 0u, 0u};
         const u32x2 z2 = {0u, 0u};
-        // Branch-free: every lane realigns (shift 0 away from row edges),
-        // masks and stores, so no wait for the loads sits under a branch.
+        if (wave_inside && full) {
+            // no lane of the wave touches a row edge and every channel is
+            // present (a full chunk): transpose and store only
+#pragma unroll
+            for (int it = 0; it < C::XITEMS; ++it) {
+                u32x4 tr[NP];
+                transpose_block(xr[it], tr);
+#pragma unroll
+                for (int p = 0; p < NP; ++p)
+                    *reinterpret_cast<u32x4*>(xs + xlds[it] + p * RSA) = tr[p];
+            }
+        } else {
+        // every lane realigns (shift 0 away from row edges) and masks
 #pragma unroll
         for (int it = 0; it < C::XITEMS; ++it) {
             const uint32_t m = xm[it];
@@ -375,9 +415,12 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
             for (int p = 0; p < NP; ++p)
                 *reinterpret_cast<u32x4*>(xs + xlds[it] + p * RSA) = (m & (1u << p)) ? tr[p] : z;
         }
+        }
+        // B rows past C_out or past the phases feed only columns that are
+        // never stored: their (finite) values need no masking
 #pragma unroll
         for (int it = 0; it < C::BITEMS; ++it)
-            *reinterpret_cast<u32x4*>(bs + blds[it]) = bval[it] ? br[it] : z;
+            *reinterpret_cast<u32x4*>(bs + blds[it]) = br[it];
     };
 
     f32x4 acc[RB][CB];
@@ -391,7 +434,7 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const int tr0 = (wm * RB + rb) * 16;
-        arow[rb] = (tr0 / TAX) * WXP + (tr0 % TAX) + li;
+        arow[rb] = (tr0 / TAX) * WXP + (tr0 % TAX) + li + a.xofs;
     }
     const int bcol = (wn * CB) * 16 + li;
 
@@ -470,33 +513,61 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
         // would make each buffer a merge of old and new registers, which the
         // compiler resolves with copies that wait for the loads in flight.
         const int c_last = c_end - 1;
-        gload(c_begin, xr0, xm0, br0);
-        gload(min(c_begin + 1, c_last), xr1, xm1, br1);
-        lstore(0, xr0, xm0, br0);
-        __syncthreads();
-        // Steady state: chunks i and i+1 with at least one more chunk after
-        // them, so every store below is unconditional (a skipped store
-        // would leave its loads "in flight" for the compiler at the loop
-        // head, where it then waits for every load).
-        int i = 0;
-        for (; i + 2 < nck; i += 2) {
-            // chunk i in stage 0; buffer 0 is free, buffer 1 holds chunk i+1
-            gload(c_begin + i + 2, xr0, xm0, br0);
+        if constexpr (C::PF == 2) {
+            gload(c_begin, xr0, xm0, br0, xf0);
+            gload(min(c_begin + 1, c_last), xr1, xm1, br1, xf1);
+            lstore(0, xr0, xm0, br0, xf0);
+            __syncthreads();
+            // Steady state: chunks i and i+1 with at least one more chunk after
+            // them, so every store below is unconditional (a skipped store
+            // would leave its loads "in flight" for the compiler at the loop
+            // head, where it then waits for every load).
+            int i = 0;
+            for (; i + 2 < nck; i += 2) {
+                // chunk i in stage 0; buffer 0 is free, buffer 1 holds chunk i+1
+                gload(c_begin + i + 2, xr0, xm0, br0, xf0);
+                compute(0);
+                lstore(1, xr1, xm1, br1, xf1);
+                __syncthreads();
+                // chunk i+1 in stage 1; buffer 1 is free, buffer 0 holds chunk i+2
+                gload(min(c_begin + i + 3, c_last), xr1, xm1, br1, xf1);
+                compute(1);
+                lstore(0, xr0, xm0, br0, xf0);
+                __syncthreads();
+            }
+            // last one or two chunks: chunk i in stage 0, chunk i+1 in buffer 1
             compute(0);
-            lstore(1, xr1, xm1, br1);
+            if (i + 1 < nck) {
+                lstore(1, xr1, xm1, br1, xf1);
+                __syncthreads();
+                compute(1);
+            }
+        } else {
+            // one register buffer: chunk c+1 is loaded during the MFMAs of
+            // chunk c and stored to the other stage after them
+            gload(c_begin, xr0, xm0, br0, xf0);
+            lstore(0, xr0, xm0, br0, xf0);
             __syncthreads();
-            // chunk i+1 in stage 1; buffer 1 is free, buffer 0 holds chunk i+2
-            gload(min(c_begin + i + 3, c_last), xr1, xm1, br1);
-            compute(1);
-            lstore(0, xr0, xm0, br0);
-            __syncthreads();
-        }
-        // last one or two chunks: chunk i in stage 0, chunk i+1 in buffer 1
-        compute(0);
-        if (i + 1 < nck) {
-            lstore(1, xr1, xm1, br1);
-            __syncthreads();
-            compute(1);
+            int i = 0;
+            for (; i + 2 < nck; i += 2) {
+                gload(c_begin + i + 1, xr0, xm0, br0, xf0);
+                compute(0);
+                lstore(1, xr0, xm0, br0, xf0);
+                __syncthreads();
+                gload(c_begin + i + 2, xr0, xm0, br0, xf0);
+                compute(1);
+                lstore(0, xr0, xm0, br0, xf0);
+                __syncthreads();
+            }
+            if (i + 1 < nck) {
+                gload(c_begin + i + 1, xr0, xm0, br0, xf0);
+                compute(0);
+                lstore(1, xr0, xm0, br0, xf0);
+                __syncthreads();
+                compute(1);
+            } else {
+                compute(0);
+            }
         }
     }
     // the output staging below reuses the operand stages: every wave must be
@@ -610,6 +681,10 @@ Inst inst_1d() {
     if constexpr (sizeof(typename TR::storage) == 2) {
         if constexpr (CTCONV_TILE_VARIANT == 1)
             return make_inst<TR, MY, MX, 128, 4, CB, 2, 2, 1>();
+        else if constexpr (CTCONV_TILE_VARIANT == 3)
+            return make_inst<TR, MY, MX, 256, 8, (CB == 5 ? 5 : (MY * MX <= 2 ? 8 : 4)), 2, 2, 1>();
+        else if constexpr (CTCONV_TILE_VARIANT == 4 && CB == 4 && MY * MX <= 2)
+            return make_inst<TR, MY, MX, 256, 4, 4, 4, 2, 2>();
         else
             return make_inst<TR, MY, MX, 256, 4, CB, 4, 2, 1>();
     } else {
@@ -622,6 +697,8 @@ Inst inst_2d() {
     if constexpr (sizeof(typename TR::storage) == 2) {
         if constexpr (CTCONV_TILE_VARIANT == 1)
             return make_inst<TR, MY, MX, 32, 4, 4, 2, 2, 1>();
+        else if constexpr (CTCONV_TILE_VARIANT == 3)
+            return make_inst<TR, MY, MX, 64, 8, (MY * MX <= 2 ? 8 : 4), 2, 2, 1>();
         else
             return make_inst<TR, MY, MX, 64, 4, 4, 4, 2, 1>();
     } else {
@@ -739,6 +816,15 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
     a->spreadx = spread_x ? 1 : 0;
     a->WY = in.TAY + (int)p.mH - 1 + a->spready;
     a->WX = in.TAX + (int)p.mW - 1 + a->spreadx;
+    {
+        // Rows a multiple of 8 bytes long start 8-byte aligned (x itself is
+        // 16-byte aligned), so a window start at a multiple of NP positions
+        // makes every x load aligned.  Tile starts are multiples of 16, so
+        // the shift is the same for every tile.
+        const int es = p.dtype == CTCONV_F32 ? 4 : 2, np = 8 / es;
+        const int w0 = a->dminx - ((int)p.mW - 1);
+        a->xofs = (p.W * es) % 8 == 0 ? ((w0 % np) + np) % np : 0;
+    }
     a->TCO = (int)TCO;
     a->PT = (int)PT;
     a->phase_subset = subset;
