@@ -786,6 +786,9 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
     const int64_t tiles_y = (Ay + in.TAY - 1) / in.TAY, tiles_x = (Ax + in.TAX - 1) / in.TAX;
     const int64_t n_row_tiles = p.N * tiles_y * tiles_x;
     const int64_t n_col_tiles = n_co_tiles * n_ph_tiles;
+    // chunks must tile the packed channel padding exactly (a chunk past it
+    // would read beyond the packed weight)
+    if (p.C_in_pad % in.KC != 0) return false;
     const int64_t n_chunks = p.C_in_pad / in.KC;
     if (n_row_tiles * n_col_tiles > kInt32Max || P > kInt32Max / 2 || p.C_out > kInt32Max / 2 ||
         Ax > kInt32Max / 2 || Ay > kInt32Max / 2 || n_chunks > kInt32Max ||
