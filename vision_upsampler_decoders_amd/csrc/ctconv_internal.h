@@ -89,6 +89,7 @@ struct PolyArgs {
     int chunks_per_split;  // split over C_in: each blockIdx.y takes this many chunks
     int atomic_out;        // 1: accumulate with fp32 atomics into a pre-filled y
     int xcd_remap;         // 1: gridDim.x is a multiple of 8, remap for L2 locality
+    uint32_t pw_bytes;     // size of the packed weight (below 2^32)
 };
 
 // Launchers (each returns hipGetLastError() of its launch).

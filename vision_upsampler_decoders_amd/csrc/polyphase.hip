@@ -94,14 +94,20 @@ struct Mma<TF32> {
 };
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2_u __attribute__((ext_vector_type(2), aligned(1)));
 
-__device__ inline u32x2 load8_unaligned(const void* p) {
-    return *reinterpret_cast<const u32x2_u*>(p);
-}
+// Fourth word of a raw (stride 0) buffer resource on gfx9-family chips:
+// 32-bit data format, no swizzle; byte offsets are range-checked against the
+// resource's size and out-of-range loads return zero.
+constexpr int kBufferWord3 = 0x00020000;
 
-__device__ inline u32x4 load16_unaligned(const void* p) {
-    return *reinterpret_cast<const u32x4_u*>(p);
+// Values that are the same in every lane, pinned to scalar registers: buffer
+// resources and scalar offsets must be, and a value the compiler cannot prove
+// uniform would otherwise cost a loop over the distinct lane values.
+__device__ inline uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline void* uniform_ptr(const void* p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    return reinterpret_cast<void*>(((uint64_t)uniform((uint32_t)(u >> 32)) << 32) |
+                                   uniform((uint32_t)u));
 }
 
 __device__ inline void store16_unaligned(void* p, const u32x4 v) {
@@ -161,7 +167,7 @@ struct Cfg {
     // global -> register prefetch depth in chunks: one wave per SIMD with a
     // 128 x 128-class wave tile has long MFMA phases but no registers for a
     // second buffer
-    static constexpr int PF = ((NW == 4 && RB * CB >= 32) || KS >= 2) ? 1 : 2;
+    static constexpr int PF = (RB * CB >= 32 || KS >= 2) ? 1 : 2;
     static_assert(BM % TAX == 0 && TAX % 16 == 0, "tile rows");
     static_assert(NW == 4 || NW == 8, "four or eight waves");
     static_assert(SMEM * ES <= 160 * 1024, "LDS");
@@ -213,30 +219,30 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
     const int ngx = WXP / NP;
     const int xitems = a.WY * ngx * NG;
     const int xper = (xitems + C::NW - 1) / C::NW;  // items per wave
-    // Per item: byte offset (within the image) of channel 0 of the group at
-    // the clamped in-row start position, the realignment shift (positions),
-    // the valid-position mask, the group's channel offset and its LDS slot.
-    uint32_t xlo[C::XITEMS];    // xgoff + xroff: the lane's offset for a full chunk
-    uint32_t xgoff[C::XITEMS];  // channel-group offset (bytes) within a chunk
-    uint32_t xroff[C::XITEMS];  // row/position offset (bytes) within a channel plane
+    // Per item: the lane's byte offset within the image (channel 0 of its
+    // group, clamped in-row start position), the realignment shift
+    // (positions), the valid-position mask and its LDS slot.
+    uint32_t xlo[C::XITEMS];
+    uint32_t xroff[C::XITEMS];  // the row/position part of xlo
+    int xg0[C::XITEMS];         // first channel of the lane's group
     int xsh[C::XITEMS];
     uint32_t xpm[C::XITEMS];
-    int xg0[C::XITEMS];
     // LDS element offset of the first position row.  Lanes without an item
     // get the 16-byte padding at the end of NP rows (never read by the
     // MFMA operand loads), spread over rows, so that every store is
     // unconditional.
     int xlds[C::XITEMS];
+    bool inside = true;  // the lane's items need no realignment or masks
 #pragma unroll
     for (int it = 0; it < C::XITEMS; ++it) {
         const int qw = lane + 64 * it;
         const int q = wave * xper + qw;
         xlds[it] = (lane % (C::XROWS / NP)) * NP * RSA + KC;
-        xgoff[it] = 0;
+        xlo[it] = 0;
         xroff[it] = 0;
+        xg0[it] = 0;
         xsh[it] = 0;
         xpm[it] = 0;
-        xg0[it] = 0;
         if (qw < xper && q < xitems) {
             const int g = q % NG;
             const int r2 = q / NG;
@@ -259,32 +265,32 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
             // no valid position is masked entirely, so its shift is irrelevant
             const int shft = p0 - p0c;
             xsh[it] = (shft > -NP && shft < NP) ? shft : 0;
-            xgoff[it] = (uint32_t)((int64_t)g * VEC * HW * C::ES);
             xroff[it] = (uint32_t)(((int64_t)(rowok ? iy : 0) * a.W + p0c) * C::ES);
             xg0[it] = g * VEC;
+            xlo[it] = (uint32_t)((int64_t)g * VEC * HW * C::ES) + xroff[it];
             xlds[it] = (wy * WXP + gx * NP) * RSA + g * VEC;
+            inside = inside && pm == (1u << NP) - 1u && xsh[it] == 0;
         }
-        xlo[it] = xgoff[it] + xroff[it];
     }
     // The whole wave's items sit inside their rows with no realignment shift
-    // (true for most tiles): its LDS stores need no shift and no masks.  Lanes
-    // without an item count as inside (they write row padding).
-    bool inside = true;
-#pragma unroll
-    for (int it = 0; it < C::XITEMS; ++it) {
-        const bool item = (wave * xper + lane + 64 * it < xitems) && (lane + 64 * it < xper);
-        inside = inside && (!item || (xpm[it] == (1u << NP) - 1u && xsh[it] == 0));
-    }
+    // (true for most tiles): its LDS stores need no shift and no masks.
     const bool wave_inside = __all(inside);
-    const char* xn = reinterpret_cast<const char*>(xg + n * a.C_in * HW);
-    const uint32_t ch_bytes = (uint32_t)(HW * C::ES);  // one channel plane
+    // Buffer resources: x of this tile's image and the packed weight.  Loads
+    // take a 32-bit lane offset plus a wave-uniform offset, and every offset
+    // stays inside the resource by construction (the hardware's range check,
+    // which zeroes out-of-range loads, is only a safety net).
+    const uint32_t ch_bytes = uniform((uint32_t)(HW * C::ES));  // one channel plane
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(xg + n * a.C_in * HW), (short)0,
+        (int)uniform(ch_bytes * (uint32_t)a.C_in), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(pwg), (short)0, (int)uniform(a.pw_bytes), kBufferWord3);
 
-    // B items: packed-weight element offset (0 for a row past C_out or past
-    // the phases: the load is made anyway so that no load sits under a
-    // branch; such rows feed only columns that are never stored) and LDS slot
-    // (row padding for lanes without one).
-    int64_t boff[C::BITEMS];
-    const char* pwb = reinterpret_cast<const char*>(pwg);
+    // B items: packed-weight byte offset (0 for a row past C_out or past the
+    // phases: the load is made anyway so that no load sits under a branch;
+    // such rows feed only columns that are never stored) and LDS slot (row
+    // padding for lanes without one).
+    uint32_t boff[C::BITEMS];
     int blds[C::BITEMS];
     constexpr int bper = (C::BMAX + C::NW - 1) / C::NW;
 #pragma unroll
@@ -300,7 +306,8 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
             if (pb < a.PT && b < a.P && co < a.C_out) {
                 const int by = b / a.sx, bx = b % a.sx;
                 const int j = ((by + a.py) % a.sy) * a.sx + (bx + a.px) % a.sx;
-                boff[it] = (((int64_t)j * a.C_out + co) * T + r) * a.C_in_pad + piece * VEC;
+                boff[it] = (uint32_t)(((((int64_t)j * a.C_out + co) * T + r) * a.C_in_pad +
+                                       piece * VEC) * C::ES);
             }
             blds[it] = (r * BN + tc) * RSA + piece * VEC;
         }
@@ -325,69 +332,49 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
     // Two register buffers: the loads of chunk c+2 are issued before the
     // MFMAs of chunk c and stored to LDS after those of chunk c+1.
     using XBuf = u32x2[C::XITEMS][VEC];
-    using XMask = uint32_t[C::XITEMS];  // bit p: position p valid; bit 8+e: channel e valid
     using BBuf = u32x4[C::BITEMS];
     XBuf xr0, xr1;
-    XMask xm0, xm1;
-    bool xf0 = true, xf1 = true;  // buffer holds a full chunk (wave-uniform)
     BBuf br0, br1;
 
     // Global -> registers.  Loads only: nothing here consumes a loaded value,
     // so no wait is needed before the MFMAs of the current chunk.  Channels
     // past C_in (ragged last chunk) load channel 0 of the group and are
     // zeroed at LDS store time, as are positions outside the row.
-    auto gload = [&](int c, XBuf& xr, XMask& xm, BBuf& br, bool& full)
-                     __attribute__((always_inline)) {
-        const int cbase = c * KC;
-        const uint32_t cbytes = (uint32_t)cbase * ch_bytes;
-        const bool cfull = cbase + KC <= a.C_in;
-        full = cfull;
-        if (cfull) {
-            // every channel present: a wave-uniform base per channel plus the
-            // lane's offset (no per-lane address arithmetic)
-            const char* xc = xn + cbytes;
+    auto gload = [&](int c, XBuf& xr, BBuf& br) __attribute__((always_inline)) {
+        const uint32_t cbase = uniform((uint32_t)c * KC);
+        if (cbase + KC <= (uint32_t)a.C_in) {
+            // every channel of the chunk exists: wave-uniform channel offsets
 #pragma unroll
-            for (int it = 0; it < C::XITEMS; ++it) {
-                xm[it] = xpm[it] | (((1u << VEC) - 1u) << 8);
+            for (int it = 0; it < C::XITEMS; ++it)
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
-                    xr[it][e] = load8_unaligned(xc + (size_t)e * ch_bytes + xlo[it]);
-            }
+                    xr[it][e] = __builtin_bit_cast(
+                        u32x2, __builtin_amdgcn_raw_buffer_load_b64(xrs, xlo[it],
+                                                                    (cbase + e) * ch_bytes, 0));
         } else {
+            // ragged last chunk: channels past C_in read channel C_in - 1
+            // (finite values that meet the packed weight's zero padding)
 #pragma unroll
-            for (int it = 0; it < C::XITEMS; ++it) {
-                // lanes without an item load channel 0 of row 0 (offsets 0)
-                // and write row padding
-                uint32_t m = xpm[it];
-#pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    m |= (cbase + xg0[it] + e < a.C_in) ? (1u << (8 + e)) : 0u;
-                xm[it] = m;
+            for (int it = 0; it < C::XITEMS; ++it)
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    // channels past C_in read channel 0 of the image (always
-                    // present) and are zeroed at store time
-                    const uint32_t off = (m & (1u << (8 + e)))
-                                             ? cbytes + xgoff[it] + e * ch_bytes + xroff[it]
-                                             : xroff[it];
-                    xr[it][e] = load8_unaligned(xn + off);
+                    const uint32_t ch = min(cbase + (uint32_t)(xg0[it] + e), (uint32_t)a.C_in - 1u);
+                    xr[it][e] = __builtin_bit_cast(
+                        u32x2, __builtin_amdgcn_raw_buffer_load_b64(xrs, ch * ch_bytes + xroff[it],
+                                                                    0, 0));
                 }
-            }
         }
 #pragma unroll
         for (int it = 0; it < C::BITEMS; ++it)
-            br[it] = *reinterpret_cast<const u32x4*>(pwb + (boff[it] + cbase) * C::ES);
+            br[it] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(brs, boff[it], cbase * C::ES, 0));
     };
-
-    auto lstore = [&](int st, const XBuf& xr, const XMask& xm, const BBuf& br, const bool full)
-                      __attribute__((always_inline)) {
+    auto lstore = [&](int st, const XBuf& xr, const BBuf& br) __attribute__((always_inline)) {
         S* xs = smem + st * C::STAGE;
         S* bs = xs + C::XROWS * RSA;
         const u32x4 z = {0u, 0u, 0u, 0u};
-        const u32x2 z2 = {0u, 0u};
-        if (wave_inside && full) {
-            // no lane of the wave touches a row edge and every channel is
-            // present (a full chunk): transpose and store only
+        if (wave_inside) {
+            // no lane of the wave touches a row edge: transpose and store only
 #pragma unroll
             for (int it = 0; it < C::XITEMS; ++it) {
                 u32x4 tr[NP];
@@ -397,24 +384,26 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
                     *reinterpret_cast<u32x4*>(xs + xlds[it] + p * RSA) = tr[p];
             }
         } else {
-        // every lane realigns (shift 0 away from row edges) and masks
+            // every lane realigns (shift 0 away from row edges) and zeroes
+            // the positions outside its row
 #pragma unroll
-        for (int it = 0; it < C::XITEMS; ++it) {
-            const uint32_t m = xm[it];
-            const int sh = xsh[it] * (int)(8 * C::ES);
-            u32x2 in[VEC];
-            u32x4 tr[NP];
+            for (int it = 0; it < C::XITEMS; ++it) {
+                const uint32_t m = xpm[it];
+                const int sh = xsh[it] * (int)(8 * C::ES);
+                u32x2 in[VEC];
+                u32x4 tr[NP];
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-                uint64_t v = __builtin_bit_cast(uint64_t, xr[it][e]);
-                v = sh >= 0 ? (v >> sh) : (v << -sh);
-                in[e] = (m & (1u << (8 + e))) ? __builtin_bit_cast(u32x2, v) : z2;
+                for (int e = 0; e < VEC; ++e) {
+                    uint64_t v = __builtin_bit_cast(uint64_t, xr[it][e]);
+                    v = sh >= 0 ? (v >> sh) : (v << -sh);
+                    in[e] = __builtin_bit_cast(u32x2, v);
+                }
+                transpose_block(in, tr);
+#pragma unroll
+                for (int p = 0; p < NP; ++p)
+                    *reinterpret_cast<u32x4*>(xs + xlds[it] + p * RSA) =
+                        (m & (1u << p)) ? tr[p] : z;
             }
-            transpose_block(in, tr);
-#pragma unroll
-            for (int p = 0; p < NP; ++p)
-                *reinterpret_cast<u32x4*>(xs + xlds[it] + p * RSA) = (m & (1u << p)) ? tr[p] : z;
-        }
         }
         // B rows past C_out or past the phases feed only columns that are
         // never stored: their (finite) values need no masking
@@ -514,9 +503,9 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
         // compiler resolves with copies that wait for the loads in flight.
         const int c_last = c_end - 1;
         if constexpr (C::PF == 2) {
-            gload(c_begin, xr0, xm0, br0, xf0);
-            gload(min(c_begin + 1, c_last), xr1, xm1, br1, xf1);
-            lstore(0, xr0, xm0, br0, xf0);
+            gload(c_begin, xr0, br0);
+            gload(min(c_begin + 1, c_last), xr1, br1);
+            lstore(0, xr0, br0);
             __syncthreads();
             // Steady state: chunks i and i+1 with at least one more chunk after
             // them, so every store below is unconditional (a skipped store
@@ -525,44 +514,44 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
             int i = 0;
             for (; i + 2 < nck; i += 2) {
                 // chunk i in stage 0; buffer 0 is free, buffer 1 holds chunk i+1
-                gload(c_begin + i + 2, xr0, xm0, br0, xf0);
+                gload(c_begin + i + 2, xr0, br0);
                 compute(0);
-                lstore(1, xr1, xm1, br1, xf1);
+                lstore(1, xr1, br1);
                 __syncthreads();
                 // chunk i+1 in stage 1; buffer 1 is free, buffer 0 holds chunk i+2
-                gload(min(c_begin + i + 3, c_last), xr1, xm1, br1, xf1);
+                gload(min(c_begin + i + 3, c_last), xr1, br1);
                 compute(1);
-                lstore(0, xr0, xm0, br0, xf0);
+                lstore(0, xr0, br0);
                 __syncthreads();
             }
             // last one or two chunks: chunk i in stage 0, chunk i+1 in buffer 1
             compute(0);
             if (i + 1 < nck) {
-                lstore(1, xr1, xm1, br1, xf1);
+                lstore(1, xr1, br1);
                 __syncthreads();
                 compute(1);
             }
         } else {
             // one register buffer: chunk c+1 is loaded during the MFMAs of
             // chunk c and stored to the other stage after them
-            gload(c_begin, xr0, xm0, br0, xf0);
-            lstore(0, xr0, xm0, br0, xf0);
+            gload(c_begin, xr0, br0);
+            lstore(0, xr0, br0);
             __syncthreads();
             int i = 0;
             for (; i + 2 < nck; i += 2) {
-                gload(c_begin + i + 1, xr0, xm0, br0, xf0);
+                gload(c_begin + i + 1, xr0, br0);
                 compute(0);
-                lstore(1, xr0, xm0, br0, xf0);
+                lstore(1, xr0, br0);
                 __syncthreads();
-                gload(c_begin + i + 2, xr0, xm0, br0, xf0);
+                gload(c_begin + i + 2, xr0, br0);
                 compute(1);
-                lstore(0, xr0, xm0, br0, xf0);
+                lstore(0, xr0, br0);
                 __syncthreads();
             }
             if (i + 1 < nck) {
-                gload(c_begin + i + 1, xr0, xm0, br0, xf0);
+                gload(c_begin + i + 1, xr0, br0);
                 compute(0);
-                lstore(1, xr0, xm0, br0, xf0);
+                lstore(1, xr0, br0);
                 __syncthreads();
                 compute(1);
             } else {
@@ -685,6 +674,8 @@ Inst inst_1d() {
             return make_inst<TR, MY, MX, 256, 8, (CB == 5 ? 5 : (MY * MX <= 2 ? 8 : 4)), 2, 2, 1>();
         else if constexpr (CTCONV_TILE_VARIANT == 4 && CB == 4 && MY * MX <= 2)
             return make_inst<TR, MY, MX, 256, 4, 4, 4, 2, 2>();
+        else if constexpr (CTCONV_TILE_VARIANT == 5 && CB == 4 && MY * MX <= 2)
+            return make_inst<TR, MY, MX, 256, 4, 8, 4, 2, 1>();
         else
             return make_inst<TR, MY, MX, 256, 4, CB, 4, 2, 1>();
     } else {
@@ -789,6 +780,9 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
     // chunks must tile the packed channel padding exactly (a chunk past it
     // would read beyond the packed weight)
     if (p.C_in_pad % in.KC != 0) return false;
+    // loads address the packed weight through a 32-bit byte offset
+    const int64_t pw_bytes = P * p.C_out * p.T * p.C_in_pad * (p.dtype == CTCONV_F32 ? 4 : 2);
+    if (pw_bytes > (int64_t)0xFFFFFFFFLL) return false;
     const int64_t n_chunks = p.C_in_pad / in.KC;
     if (n_row_tiles * n_col_tiles > kInt32Max || P > kInt32Max / 2 || p.C_out > kInt32Max / 2 ||
         Ax > kInt32Max / 2 || Ay > kInt32Max / 2 || n_chunks > kInt32Max ||
@@ -863,6 +857,7 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
     a->chunks_per_split = (int)((n_chunks + best - 1) / best);
     a->atomic_out = best > 1 ? 1 : 0;
     a->xcd_remap = (tiles % 8 == 0) ? 1 : 0;
+    a->pw_bytes = (uint32_t)pw_bytes;
     *inst = in;
     *splits = best;
     return true;
