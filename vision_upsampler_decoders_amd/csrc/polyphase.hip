@@ -45,6 +45,8 @@
 // few tiles split the C_in reduction across workgroups (fp32 output only) and
 // accumulate with fp32 atomics into a bias-filled y.
 
+#include <type_traits>
+
 #include "ctconv_internal.h"
 
 namespace ctconv {
@@ -223,8 +225,6 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
     // group, clamped in-row start position), the realignment shift
     // (positions), the valid-position mask and its LDS slot.
     uint32_t xlo[C::XITEMS];
-    uint32_t xroff[C::XITEMS];  // the row/position part of xlo
-    int xg0[C::XITEMS];         // first channel of the lane's group
     int xsh[C::XITEMS];
     uint32_t xpm[C::XITEMS];
     // LDS element offset of the first position row.  Lanes without an item
@@ -239,8 +239,6 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
         const int q = wave * xper + qw;
         xlds[it] = (lane % (C::XROWS / NP)) * NP * RSA + KC;
         xlo[it] = 0;
-        xroff[it] = 0;
-        xg0[it] = 0;
         xsh[it] = 0;
         xpm[it] = 0;
         if (qw < xper && q < xitems) {
@@ -265,9 +263,8 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
             // no valid position is masked entirely, so its shift is irrelevant
             const int shft = p0 - p0c;
             xsh[it] = (shft > -NP && shft < NP) ? shft : 0;
-            xroff[it] = (uint32_t)(((int64_t)(rowok ? iy : 0) * a.W + p0c) * C::ES);
-            xg0[it] = g * VEC;
-            xlo[it] = (uint32_t)((int64_t)g * VEC * HW * C::ES) + xroff[it];
+            xlo[it] = (uint32_t)(((int64_t)g * VEC * HW + (int64_t)(rowok ? iy : 0) * a.W + p0c) *
+                                 C::ES);
             xlds[it] = (wy * WXP + gx * NP) * RSA + g * VEC;
             inside = inside && pm == (1u << NP) - 1u && xsh[it] == 0;
         }
@@ -276,9 +273,8 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
     // (true for most tiles): its LDS stores need no shift and no masks.
     const bool wave_inside = __all(inside);
     // Buffer resources: x of this tile's image and the packed weight.  Loads
-    // take a 32-bit lane offset plus a wave-uniform offset, and every offset
-    // stays inside the resource by construction (the hardware's range check,
-    // which zeroes out-of-range loads, is only a safety net).
+    // take a 32-bit lane offset plus a wave-uniform offset; the resource's
+    // size bounds every access (out-of-range dwords read as zero, no fault).
     const uint32_t ch_bytes = uniform((uint32_t)(HW * C::ES));  // one channel plane
     const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
         uniform_ptr(xg + n * a.C_in * HW), (short)0,
@@ -342,38 +338,31 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
     // zeroed at LDS store time, as are positions outside the row.
     auto gload = [&](int c, XBuf& xr, BBuf& br) __attribute__((always_inline)) {
         const uint32_t cbase = uniform((uint32_t)c * KC);
-        if (cbase + KC <= (uint32_t)a.C_in) {
-            // every channel of the chunk exists: wave-uniform channel offsets
+        // Channels past C_in (ragged last chunk) start at or past the end of
+        // the image's resource, so the hardware returns zeros for them: the
+        // range check of a raw buffer load covers the scalar offset too and
+        // zeroes each out-of-range dword (checked on gfx950), so every chunk
+        // uses the same load form and no load sits under a branch.
 #pragma unroll
-            for (int it = 0; it < C::XITEMS; ++it)
+        for (int it = 0; it < C::XITEMS; ++it)
 #pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    xr[it][e] = __builtin_bit_cast(
-                        u32x2, __builtin_amdgcn_raw_buffer_load_b64(xrs, xlo[it],
-                                                                    (cbase + e) * ch_bytes, 0));
-        } else {
-            // ragged last chunk: channels past C_in read channel C_in - 1
-            // (finite values that meet the packed weight's zero padding)
-#pragma unroll
-            for (int it = 0; it < C::XITEMS; ++it)
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) {
-                    const uint32_t ch = min(cbase + (uint32_t)(xg0[it] + e), (uint32_t)a.C_in - 1u);
-                    xr[it][e] = __builtin_bit_cast(
-                        u32x2, __builtin_amdgcn_raw_buffer_load_b64(xrs, ch * ch_bytes + xroff[it],
-                                                                    0, 0));
-                }
-        }
+            for (int e = 0; e < VEC; ++e)
+                xr[it][e] = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(xrs, xlo[it],
+                                                                (cbase + e) * ch_bytes, 0));
 #pragma unroll
         for (int it = 0; it < C::BITEMS; ++it)
             br[it] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(brs, boff[it], cbase * C::ES, 0));
     };
-    auto lstore = [&](int st, const XBuf& xr, const BBuf& br) __attribute__((always_inline)) {
+    // `inside`: true_type when the caller knows that no item of the wave needs
+    // realignment or masks, false_type to decide from wave_inside at run time
+    auto lstore = [&](int st, const XBuf& xr, const BBuf& br, auto inside)
+                      __attribute__((always_inline)) {
         S* xs = smem + st * C::STAGE;
         S* bs = xs + C::XROWS * RSA;
         const u32x4 z = {0u, 0u, 0u, 0u};
-        if (wave_inside) {
+        if (decltype(inside)::value || wave_inside) {
             // no lane of the wave touches a row edge: transpose and store only
 #pragma unroll
             for (int it = 0; it < C::XITEMS; ++it) {
@@ -493,6 +482,54 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
     };
 
     // ---- main loop over input-channel chunks (two chunks per iteration) ----
+    // Waves whose column blocks all share one shift class (every wave of a
+    // shape whose phases split into classes along the wave boundaries) run a
+    // branch-free chunk step: per tap its A and B fragments and MFMAs, with the
+    // next chunk's global loads and the other stage's LDS stores issued right
+    // after the first tap so that they overlap the remaining MFMAs.
+    const bool single = (clsmask & (clsmask - 1u)) == 0u;
+    const int c0 = __builtin_ctz(clsmask);
+    int arow1[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) arow1[rb] = arow[rb] + (Y2 ? (c0 >> 1) * WXP : 0) + (c0 & 1);
+    // `pre` (the next chunk's global loads) is issued first and `mid` (the
+    // other stage's LDS stores, which wait for loads issued one step earlier)
+    // after the first tap; scheduling barriers keep the compiler from moving
+    // the loads late and their consumers early, which would expose the full
+    // memory latency at every step.
+    auto fused = [&](int st, auto&& pre, auto&& mid) __attribute__((always_inline)) {
+        const S* xs = smem + st * C::STAGE;
+        const S* bs = xs + C::XROWS * RSA;
+        pre();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int kofs = ks * C::KSTEP + lg * VEC;
+#pragma unroll
+            for (int r = 0; r < T; ++r) {
+                const int ry = r / MX, rx = r % MX;
+                u32x4 afr[RB], bfr[CB];
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+                    afr[rb] = *reinterpret_cast<const u32x4*>(
+                        xs + (arow1[rb] + (MY - 1 - ry) * WXP + (MX - 1 - rx)) * RSA + kofs);
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+                    bfr[cb] = *reinterpret_cast<const u32x4*>(
+                        bs + (r * BN + bcol + cb * 16) * RSA + kofs);
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+                        Mma<TR>::step(acc[rb][cb], afr[rb], bfr[cb]);
+                if (ks == 0 && r == 0) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    mid();
+                }
+            }
+        }
+    };
+
     const int c_begin = blockIdx.y * a.chunks_per_split;
     const int c_end = min(c_begin + a.chunks_per_split, a.n_chunks);
     const int nck = c_end - c_begin;
@@ -502,10 +539,50 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
         // would make each buffer a merge of old and new registers, which the
         // compiler resolves with copies that wait for the loads in flight.
         const int c_last = c_end - 1;
-        if constexpr (C::PF == 2) {
+        // (the fused step keeps both buffers and a tap's fragments live: only
+        // instances with at most 8 B fragments per k-step fit without spills)
+        if (C::PF == 2 && CB * T <= 8 && single) {
+            // two copies of the loop: with and without edge handling in the
+            // LDS stores, so that the chunk step has no branch
+            auto run = [&](auto inside) __attribute__((always_inline)) {
+                gload(c_begin, xr0, br0);
+                gload(min(c_begin + 1, c_last), xr1, br1);
+                lstore(0, xr0, br0, inside);
+                __syncthreads();
+                int i = 0;
+                for (; i + 2 < nck; i += 2) {
+                    // chunk i in stage 0, chunk i+1 in buffer 1; buffer 0 is free
+                    fused(
+                        0, [&]() __attribute__((always_inline)) { gload(c_begin + i + 2, xr0, br0); },
+                        [&]() __attribute__((always_inline)) { lstore(1, xr1, br1, inside); });
+                    __syncthreads();
+                    // chunk i+1 in stage 1, chunk i+2 in buffer 0; buffer 1 is free
+                    fused(
+                        1,
+                        [&]() __attribute__((always_inline)) {
+                            gload(min(c_begin + i + 3, c_last), xr1, br1);
+                        },
+                        [&]() __attribute__((always_inline)) { lstore(0, xr0, br0, inside); });
+                    __syncthreads();
+                }
+                if (i + 1 < nck) {
+                    fused(
+                        0, []() {},
+                        [&]() __attribute__((always_inline)) { lstore(1, xr1, br1, inside); });
+                    __syncthreads();
+                    fused(1, []() {}, []() {});
+                } else {
+                    fused(0, []() {}, []() {});
+                }
+            };
+            if (wave_inside)
+                run(std::true_type{});
+            else
+                run(std::false_type{});
+        } else if constexpr (C::PF == 2) {
             gload(c_begin, xr0, br0);
             gload(min(c_begin + 1, c_last), xr1, br1);
-            lstore(0, xr0, br0);
+            lstore(0, xr0, br0, std::false_type{});
             __syncthreads();
             // Steady state: chunks i and i+1 with at least one more chunk after
             // them, so every store below is unconditional (a skipped store
@@ -516,18 +593,18 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
                 // chunk i in stage 0; buffer 0 is free, buffer 1 holds chunk i+1
                 gload(c_begin + i + 2, xr0, br0);
                 compute(0);
-                lstore(1, xr1, br1);
+                lstore(1, xr1, br1, std::false_type{});
                 __syncthreads();
                 // chunk i+1 in stage 1; buffer 1 is free, buffer 0 holds chunk i+2
                 gload(min(c_begin + i + 3, c_last), xr1, br1);
                 compute(1);
-                lstore(0, xr0, br0);
+                lstore(0, xr0, br0, std::false_type{});
                 __syncthreads();
             }
             // last one or two chunks: chunk i in stage 0, chunk i+1 in buffer 1
             compute(0);
             if (i + 1 < nck) {
-                lstore(1, xr1, br1);
+                lstore(1, xr1, br1, std::false_type{});
                 __syncthreads();
                 compute(1);
             }
@@ -535,23 +612,23 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
             // one register buffer: chunk c+1 is loaded during the MFMAs of
             // chunk c and stored to the other stage after them
             gload(c_begin, xr0, br0);
-            lstore(0, xr0, br0);
+            lstore(0, xr0, br0, std::false_type{});
             __syncthreads();
             int i = 0;
             for (; i + 2 < nck; i += 2) {
                 gload(c_begin + i + 1, xr0, br0);
                 compute(0);
-                lstore(1, xr0, br0);
+                lstore(1, xr0, br0, std::false_type{});
                 __syncthreads();
                 gload(c_begin + i + 2, xr0, br0);
                 compute(1);
-                lstore(0, xr0, br0);
+                lstore(0, xr0, br0, std::false_type{});
                 __syncthreads();
             }
             if (i + 1 < nck) {
                 gload(c_begin + i + 1, xr0, br0);
                 compute(0);
-                lstore(1, xr0, br0);
+                lstore(1, xr0, br0, std::false_type{});
                 __syncthreads();
                 compute(1);
             } else {
