@@ -648,31 +648,100 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
     // hold consecutive output channels, so an unpadded power-of-two stride
     // would put all 16 of their staging writes in one LDS bank
     const int CSTR = R * SS + VEC;
+    // Column block cb holds 16 consecutive output channels of one phase when
+    // TCO is a multiple of 16 (every shape but the narrow and phase-subset
+    // ones): its phase, channel base and row offsets are wave-uniform, and
+    // block cb + TCO/16 holds the next phase of the same channels, i.e. the
+    // next output element of a row, so the two values go out as one 4-byte
+    // LDS write when both phases sit in the same output row.
+    auto stage_pairs = [&](auto step_tag) __attribute__((always_inline)) {
+        constexpr int STEP = decltype(step_tag)::value;  // TCO / 16 (0: no pairing)
+        const int T0 = wm * RB * 16;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-        const int tc = bcol + cb * 16;
-        const int pb = tc / a.TCO, co_l = tc - (tc / a.TCO) * a.TCO;
-        if (pb >= a.PT) continue;
-        const int co = co0 + co_l;
-        float bv = 0.f;
-        if (!a.atomic_out && biasg != nullptr && co < a.C_out) bv = TR::to_f32(biasg[co]);
-        const int by = pb / a.sx, bx = pb - by * a.sx;
+        for (int cb = 0; cb < CB; ++cb) {
+            const int blk = wn * CB + cb;
+            const int pb = (int)uniform((uint32_t)(blk * 16 / a.TCO));
+            if (pb >= a.PT) continue;
+            const int co_l = blk * 16 - pb * a.TCO + li;
+            const int by = pb / a.sx, bx = pb - by * a.sx;
+            // Blocks pair up as (cb, cb + STEP) for (cb / STEP) even; a pair is
+            // written together when the second block exists in the wave, holds
+            // a phase of the tile and that phase continues the same output row.
+            constexpr bool CAN = STEP > 0 && STEP < CB;
+            const bool first = CAN && ((cb / (CAN ? STEP : 1)) % 2 == 0) && cb + STEP < CB;
+            const bool second = CAN && ((cb / (CAN ? STEP : 1)) % 2 == 1);
+            const int cbp = first ? cb + STEP : cb;
+            const bool pair = first && pb + 1 < a.PT && bx + 1 < a.sx;
+            if (second && (pb - 1) - ((pb - 1) / a.sx) * a.sx + 1 < a.sx)
+                continue;  // written together with the previous phase's block
+            const int co = co0 + co_l;
+            float bv = 0.f;
+            if (!a.atomic_out && biasg != nullptr && co < a.C_out) bv = TR::to_f32(biasg[co]);
+            const int lane_base = co_l * CSTR + lg * 4 * a.sx + bx;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+            for (int rb = 0; rb < RB; ++rb) {
+                const int t = T0 + rb * 16;
+                const int rowpart = ((t / TAX) * a.sy + by) * SS + (t % TAX) * a.sx;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tr = (wm * RB + rb) * 16 + lg * 4 + i;
-                const int ayl = tr / TAX, axl = tr % TAX;
-                int rr, ss;
-                if (a.phase_subset) {
-                    rr = axl;
-                    ss = pb;
-                } else {
-                    rr = ayl * a.sy + by;
-                    ss = axl * a.sx + bx;
+                for (int i = 0; i < 4; ++i) {
+                    S* dst = smem + lane_base + rowpart + i * a.sx;
+                    const S v0 = TR::from_f32(acc[rb][cb][i] + bv);
+                    if (pair) {
+                        const S v1 = TR::from_f32(acc[rb][cbp][i] + bv);
+                        if constexpr (sizeof(S) == 2) {
+                            // 4-byte aligned: output rows and phase pairs start even
+                            const uint32_t w = (uint32_t)__builtin_bit_cast(uint16_t, v0) |
+                                               ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
+                            if ((((uintptr_t)dst) & 3u) == 0u) {
+                                *reinterpret_cast<uint32_t*>(dst) = w;
+                            } else {
+                                dst[0] = v0;
+                                dst[1] = v1;
+                            }
+                        } else {
+                            dst[0] = v0;
+                            dst[1] = v1;
+                        }
+                    } else {
+                        *dst = v0;
+                    }
                 }
-                smem[co_l * CSTR + rr * SS + ss] = TR::from_f32(acc[rb][cb][i] + bv);
             }
+        }
+    };
+    if (!a.phase_subset && (a.TCO & 15) == 0 && a.TCO / 16 == 1) {
+        stage_pairs(std::integral_constant<int, 1>{});
+    } else if (!a.phase_subset && (a.TCO & 15) == 0 && a.TCO / 16 == 2) {
+        stage_pairs(std::integral_constant<int, 2>{});
+    } else if (!a.phase_subset && (a.TCO & 15) == 0) {
+        stage_pairs(std::integral_constant<int, 0>{});
+    } else {
+    #pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const int tc = bcol + cb * 16;
+            const int pb = tc / a.TCO, co_l = tc - (tc / a.TCO) * a.TCO;
+            if (pb >= a.PT) continue;
+            const int co = co0 + co_l;
+            float bv = 0.f;
+            if (!a.atomic_out && biasg != nullptr && co < a.C_out) bv = TR::to_f32(biasg[co]);
+            const int by = pb / a.sx, bx = pb - by * a.sx;
+    #pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tr = (wm * RB + rb) * 16 + lg * 4 + i;
+                    const int ayl = tr / TAX, axl = tr % TAX;
+                    int rr, ss;
+                    if (a.phase_subset) {
+                        rr = axl;
+                        ss = pb;
+                    } else {
+                        rr = ayl * a.sy + by;
+                        ss = axl * a.sx + bx;
+                    }
+                    smem[co_l * CSTR + rr * SS + ss] = TR::from_f32(acc[rb][cb][i] + bv);
+                }
+        }
     }
     __syncthreads();
 
