@@ -805,9 +805,10 @@ Inst make_inst() {
                 C::KC, C::NT, (int)(C::SMEM * C::ES)};
 }
 
-// Tile shapes.  16-bit storage: 256 output rows x 128 (or 160 for five phases)
-// columns, eight waves of 64 x 64 (64 x 80) each, two per SIMD, one workgroup
-// per CU.  fp32: 128 x 128 with eight waves of 64 x 32.
+// Tile shapes.  16-bit storage: 256 output rows x 128 columns, eight waves of
+// 64 x 64 each, two per SIMD, one workgroup per CU; five-phase shapes: 128 x
+// 160 with four waves of 64 x 80, two workgroups per CU.  fp32: 128 x 128
+// with eight waves of 64 x 32.
 #ifndef CTCONV_TILE_VARIANT
 #define CTCONV_TILE_VARIANT 2
 #endif
@@ -822,6 +823,10 @@ Inst inst_1d() {
             return make_inst<TR, MY, MX, 256, 4, 4, 4, 2, 2>();
         else if constexpr (CTCONV_TILE_VARIANT == 5 && CB == 4 && MY * MX <= 2)
             return make_inst<TR, MY, MX, 256, 4, 8, 4, 2, 1>();
+        else if constexpr (CB == 5)
+            // five-phase column tiles do not take the fused step; two 4-wave
+            // workgroups per CU overlap one's epilogue with the other's loop
+            return make_inst<TR, MY, MX, 128, 4, 5, 2, 2, 1>();
         else
             return make_inst<TR, MY, MX, 256, 4, CB, 4, 2, 1>();
     } else {
