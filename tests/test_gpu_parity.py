@@ -126,6 +126,10 @@ FULL_CASES = [
     ("len2_f32", "f32", 3, 40, 16, (2,), (8,), (4,), (2,), (0,), (1,), True),
     ("len4_bf16", "bf16", 3, 40, 24, (4,), (8,), (4,), (3,), (0,), (1,), True),
     ("w4_2d_bf16", "bf16", 2, 32, 16, (5, 4), (4, 4), (2, 2), (1, 1), (0, 0), (1, 1), True),
+    # odd input rows (2-byte-offset row pieces): odd length with ragged
+    # channels, and a 2-D plane of odd size (odd channels 2 bytes off)
+    ("odd_len_bf16", "bf16", 2, 40, 24, (301,), (8,), (4,), (2,), (0,), (1,), True),
+    ("odd_plane_2d_bf16", "bf16", 2, 36, 16, (5, 7), (4, 4), (2, 2), (1, 1), (0, 0), (1, 1), True),
 ]
 
 

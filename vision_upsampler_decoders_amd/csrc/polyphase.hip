@@ -96,6 +96,7 @@ struct Mma<TF32> {
 };
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 // Fourth word of a raw (stride 0) buffer resource on gfx9-family chips:
 // 32-bit data format, no swizzle; byte offsets are range-checked against the
@@ -175,7 +176,11 @@ struct Cfg {
     static_assert(SMEM * ES <= 160 * 1024, "LDS");
 };
 
-template <class TR, int MY, int MX, int TAX, int RB, int CB, int WM, int WN, int KS>
+// XODD: 16-bit input rows of odd length.  Row pieces then start at 2-byte
+// offsets in every other channel plane or row; each piece is loaded as the 12
+// dword-aligned bytes that contain it and extracted at LDS-store time (a
+// 2-byte-misaligned 8-byte load costs the texture path per lane).
+template <class TR, int MY, int MX, int TAX, int RB, int CB, int WM, int WN, int KS, bool XODD>
 __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
     using C = Cfg<TR, MY, MX, TAX, RB, CB, WM, WN, KS>;
     using S = typename TR::storage;
@@ -225,6 +230,8 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
     // group, clamped in-row start position), the realignment shift
     // (positions), the valid-position mask and its LDS slot.
     uint32_t xlo[C::XITEMS];
+    uint32_t xv0[XODD ? C::XITEMS : 1], xs0[XODD ? C::XITEMS : 1];
+    uint32_t xv1[XODD ? C::XITEMS : 1], xs1[XODD ? C::XITEMS : 1];
     int xsh[C::XITEMS];
     uint32_t xpm[C::XITEMS];
     // LDS element offset of the first position row.  Lanes without an item
@@ -239,6 +246,12 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
         const int q = wave * xper + qw;
         xlds[it] = (lane % (C::XROWS / NP)) * NP * RSA + KC;
         xlo[it] = 0;
+        if constexpr (XODD) {
+            xv0[it] = 0;
+            xs0[it] = 0;
+            xv1[it] = 0;
+            xs1[it] = 0;
+        }
         xsh[it] = 0;
         xpm[it] = 0;
         if (qw < xper && q < xitems) {
@@ -265,6 +278,14 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
             xsh[it] = (shft > -NP && shft < NP) ? shft : 0;
             xlo[it] = (uint32_t)(((int64_t)g * VEC * HW + (int64_t)(rowok ? iy : 0) * a.W + p0c) *
                                  C::ES);
+            if constexpr (XODD) {
+                // dword-aligned start and bit shift of the piece, for channel
+                // planes at even and at odd 2-byte offsets
+                xv0[it] = xlo[it] & ~3u;
+                xs0[it] = (xlo[it] & 2u) * 8u;
+                xv1[it] = (xlo[it] + 2u) & ~3u;
+                xs1[it] = ((xlo[it] + 2u) & 2u) * 8u;
+            }
             xlds[it] = (wy * WXP + gx * NP) * RSA + g * VEC;
             inside = inside && pm == (1u << NP) - 1u && xsh[it] == 0;
         }
@@ -276,6 +297,7 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
     // take a 32-bit lane offset plus a wave-uniform offset; the resource's
     // size bounds every access (out-of-range dwords read as zero, no fault).
     const uint32_t ch_bytes = uniform((uint32_t)(HW * C::ES));  // one channel plane
+    const bool odd_plane = (ch_bytes & 2u) != 0u;
     const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
         uniform_ptr(xg + n * a.C_in * HW), (short)0,
         (int)uniform(ch_bytes * (uint32_t)a.C_in), kBufferWord3);
@@ -327,7 +349,8 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
 
     // Two register buffers: the loads of chunk c+2 are issued before the
     // MFMAs of chunk c and stored to LDS after those of chunk c+1.
-    using XBuf = u32x2[C::XITEMS][VEC];
+    using XEl = std::conditional_t<XODD, u32x3, u32x2>;
+    using XBuf = XEl[C::XITEMS][VEC];
     using BBuf = u32x4[C::BITEMS];
     XBuf xr0, xr1;
     BBuf br0, br1;
@@ -346,10 +369,22 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
 #pragma unroll
         for (int it = 0; it < C::XITEMS; ++it)
 #pragma unroll
-            for (int e = 0; e < VEC; ++e)
-                xr[it][e] = __builtin_bit_cast(
-                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(xrs, xlo[it],
-                                                                (cbase + e) * ch_bytes, 0));
+            for (int e = 0; e < VEC; ++e) {
+                if constexpr (XODD) {
+                    // odd channels sit 2 bytes off the even ones when a plane
+                    // is 2 mod 4 bytes long; their scalar offset drops by 2 so
+                    // that it stays a multiple of 4
+                    const bool par = (e & 1) && odd_plane;
+                    xr[it][e] = __builtin_bit_cast(
+                        u32x3, __builtin_amdgcn_raw_buffer_load_b96(
+                                   xrs, par ? xv1[it] : xv0[it],
+                                   (cbase + e) * ch_bytes - (par ? 2u : 0u), 0));
+                } else {
+                    xr[it][e] = __builtin_bit_cast(
+                        u32x2, __builtin_amdgcn_raw_buffer_load_b64(xrs, xlo[it],
+                                                                    (cbase + e) * ch_bytes, 0));
+                }
+            }
 #pragma unroll
         for (int it = 0; it < C::BITEMS; ++it)
             br[it] = __builtin_bit_cast(
@@ -362,12 +397,30 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
         S* xs = smem + st * C::STAGE;
         S* bs = xs + C::XROWS * RSA;
         const u32x4 z = {0u, 0u, 0u, 0u};
+        // the 8-byte pieces of item `it` (odd rows: extracted from the 12
+        // loaded bytes at the piece's 2-byte offset)
+        auto pieces = [&](int it, u32x2 (&in)[VEC]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                if constexpr (XODD) {
+                    const bool par = (e & 1) && odd_plane;
+                    const uint32_t sh = par ? xs1[it] : xs0[it];
+                    const u32x3 w = xr[it][e];
+                    in[e] = u32x2{__builtin_amdgcn_alignbit(w[1], w[0], sh),
+                                  __builtin_amdgcn_alignbit(w[2], w[1], sh)};
+                } else {
+                    in[e] = xr[it][e];
+                }
+            }
+        };
         if (decltype(inside)::value || wave_inside) {
             // no lane of the wave touches a row edge: transpose and store only
 #pragma unroll
             for (int it = 0; it < C::XITEMS; ++it) {
+                u32x2 in[VEC];
                 u32x4 tr[NP];
-                transpose_block(xr[it], tr);
+                pieces(it, in);
+                transpose_block(in, tr);
 #pragma unroll
                 for (int p = 0; p < NP; ++p)
                     *reinterpret_cast<u32x4*>(xs + xlds[it] + p * RSA) = tr[p];
@@ -381,9 +434,10 @@ __global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
                 const int sh = xsh[it] * (int)(8 * C::ES);
                 u32x2 in[VEC];
                 u32x4 tr[NP];
+                pieces(it, in);
 #pragma unroll
                 for (int e = 0; e < VEC; ++e) {
-                    uint64_t v = __builtin_bit_cast(uint64_t, xr[it][e]);
+                    uint64_t v = __builtin_bit_cast(uint64_t, in[e]);
                     v = sh >= 0 ? (v >> sh) : (v << -sh);
                     in[e] = __builtin_bit_cast(u32x2, v);
                 }
@@ -798,10 +852,11 @@ struct Inst {
     int BM, BN, TAX, TAY, KC, threads, lds_bytes;
 };
 
-template <class TR, int MY, int MX, int TAX, int RB, int CB, int WM, int WN, int KS>
+template <class TR, int MY, int MX, int TAX, int RB, int CB, int WM, int WN, int KS,
+          bool XODD = false>
 Inst make_inst() {
     using C = Cfg<TR, MY, MX, TAX, RB, CB, WM, WN, KS>;
-    return Inst{&poly_kernel<TR, MY, MX, TAX, RB, CB, WM, WN, KS>, C::BM, C::BN, TAX, C::TAY,
+    return Inst{&poly_kernel<TR, MY, MX, TAX, RB, CB, WM, WN, KS, XODD>, C::BM, C::BN, TAX, C::TAY,
                 C::KC, C::NT, (int)(C::SMEM * C::ES)};
 }
 
@@ -812,67 +867,77 @@ Inst make_inst() {
 #ifndef CTCONV_TILE_VARIANT
 #define CTCONV_TILE_VARIANT 2
 #endif
-template <class TR, int MY, int MX, int CB>
+template <class TR, int MY, int MX, int CB, bool XO>
 Inst inst_1d() {
     if constexpr (sizeof(typename TR::storage) == 2) {
         if constexpr (CTCONV_TILE_VARIANT == 1)
-            return make_inst<TR, MY, MX, 128, 4, CB, 2, 2, 1>();
+            return make_inst<TR, MY, MX, 128, 4, CB, 2, 2, 1, XO>();
         else if constexpr (CTCONV_TILE_VARIANT == 3)
-            return make_inst<TR, MY, MX, 256, 8, (CB == 5 ? 5 : (MY * MX <= 2 ? 8 : 4)), 2, 2, 1>();
+            return make_inst<TR, MY, MX, 256, 8, (CB == 5 ? 5 : (MY * MX <= 2 ? 8 : 4)), 2, 2, 1, XO>();
         else if constexpr (CTCONV_TILE_VARIANT == 4 && CB == 4 && MY * MX <= 2)
-            return make_inst<TR, MY, MX, 256, 4, 4, 4, 2, 2>();
+            return make_inst<TR, MY, MX, 256, 4, 4, 4, 2, 2, XO>();
         else if constexpr (CTCONV_TILE_VARIANT == 5 && CB == 4 && MY * MX <= 2)
-            return make_inst<TR, MY, MX, 256, 4, 8, 4, 2, 1>();
+            return make_inst<TR, MY, MX, 256, 4, 8, 4, 2, 1, XO>();
         else if constexpr (CB == 5)
             // five-phase column tiles do not take the fused step; two 4-wave
             // workgroups per CU overlap one's epilogue with the other's loop
-            return make_inst<TR, MY, MX, 128, 4, 5, 2, 2, 1>();
+            return make_inst<TR, MY, MX, 128, 4, 5, 2, 2, 1, XO>();
         else
-            return make_inst<TR, MY, MX, 256, 4, CB, 4, 2, 1>();
+            return make_inst<TR, MY, MX, 256, 4, CB, 4, 2, 1, XO>();
     } else {
-        return make_inst<TR, MY, MX, 128, 4, 2, 2, 4, 1>();
+        return make_inst<TR, MY, MX, 128, 4, 2, 2, 4, 1, XO>();
     }
 }
 
-template <class TR, int MY, int MX>
+template <class TR, int MY, int MX, bool XO>
 Inst inst_2d() {
     if constexpr (sizeof(typename TR::storage) == 2) {
         if constexpr (CTCONV_TILE_VARIANT == 1)
-            return make_inst<TR, MY, MX, 32, 4, 4, 2, 2, 1>();
+            return make_inst<TR, MY, MX, 32, 4, 4, 2, 2, 1, XO>();
         else if constexpr (CTCONV_TILE_VARIANT == 3)
-            return make_inst<TR, MY, MX, 64, 8, (MY * MX <= 2 ? 8 : 4), 2, 2, 1>();
+            return make_inst<TR, MY, MX, 64, 8, (MY * MX <= 2 ? 8 : 4), 2, 2, 1, XO>();
         else
-            return make_inst<TR, MY, MX, 64, 4, 4, 4, 2, 1>();
+            return make_inst<TR, MY, MX, 64, 4, 4, 4, 2, 1, XO>();
     } else {
-        return make_inst<TR, MY, MX, 32, 4, 2, 2, 4, 1>();
+        return make_inst<TR, MY, MX, 32, 4, 2, 2, 4, 1, XO>();
     }
 }
 
-template <class TR>
-bool pick_inst(const Problem& p, int CB, Inst* out) {
+template <class TR, bool XO>
+bool pick_inst_x(const Problem& p, int CB, Inst* out) {
     if (p.ndim == 1) {
         if (CB == 5 && sizeof(typename TR::storage) == 2) {
             switch (p.mW) {
-                case 1: *out = inst_1d<TR, 1, 1, 5>(); return true;
-                case 2: *out = inst_1d<TR, 1, 2, 5>(); return true;
-                case 3: *out = inst_1d<TR, 1, 3, 5>(); return true;
-                case 4: *out = inst_1d<TR, 1, 4, 5>(); return true;
+                case 1: *out = inst_1d<TR, 1, 1, 5, XO>(); return true;
+                case 2: *out = inst_1d<TR, 1, 2, 5, XO>(); return true;
+                case 3: *out = inst_1d<TR, 1, 3, 5, XO>(); return true;
+                case 4: *out = inst_1d<TR, 1, 4, 5, XO>(); return true;
             }
             return false;
         }
         switch (p.mW) {
-            case 1: *out = inst_1d<TR, 1, 1, 4>(); return true;
-            case 2: *out = inst_1d<TR, 1, 2, 4>(); return true;
-            case 3: *out = inst_1d<TR, 1, 3, 4>(); return true;
-            case 4: *out = inst_1d<TR, 1, 4, 4>(); return true;
+            case 1: *out = inst_1d<TR, 1, 1, 4, XO>(); return true;
+            case 2: *out = inst_1d<TR, 1, 2, 4, XO>(); return true;
+            case 3: *out = inst_1d<TR, 1, 3, 4, XO>(); return true;
+            case 4: *out = inst_1d<TR, 1, 4, 4, XO>(); return true;
         }
         return false;
     }
-    if (p.mH == 1 && p.mW == 1) { *out = inst_2d<TR, 1, 1>(); return true; }
-    if (p.mH == 1 && p.mW == 2) { *out = inst_2d<TR, 1, 2>(); return true; }
-    if (p.mH == 2 && p.mW == 1) { *out = inst_2d<TR, 2, 1>(); return true; }
-    if (p.mH == 2 && p.mW == 2) { *out = inst_2d<TR, 2, 2>(); return true; }
+    if (p.mH == 1 && p.mW == 1) { *out = inst_2d<TR, 1, 1, XO>(); return true; }
+    if (p.mH == 1 && p.mW == 2) { *out = inst_2d<TR, 1, 2, XO>(); return true; }
+    if (p.mH == 2 && p.mW == 1) { *out = inst_2d<TR, 2, 1, XO>(); return true; }
+    if (p.mH == 2 && p.mW == 2) { *out = inst_2d<TR, 2, 2, XO>(); return true; }
     return false;
+}
+
+// 16-bit types with odd input rows take the XODD instances; fp32 pieces are
+// always dword aligned
+template <class TR>
+bool pick_inst(const Problem& p, int CB, Inst* out) {
+    if constexpr (sizeof(typename TR::storage) == 2) {
+        if (p.W % 2 == 1) return pick_inst_x<TR, true>(p, CB, out);
+    }
+    return pick_inst_x<TR, false>(p, CB, out);
 }
 
 bool get_inst(const Problem& p, int CB, Inst* out) {
