@@ -180,8 +180,11 @@ struct Cfg {
 // offsets in every other channel plane or row; each piece is loaded as the 12
 // dword-aligned bytes that contain it and extracted at LDS-store time (a
 // 2-byte-misaligned 8-byte load costs the texture path per lane).
+// At least two waves per SIMD (256 registers per wave): an 8-wave workgroup
+// per CU, or two 4-wave ones; only 128 x 128 wave tiles need the whole file.
 template <class TR, int MY, int MX, int TAX, int RB, int CB, int WM, int WN, int KS, bool XODD>
-__global__ __launch_bounds__(64 * WM * WN) void poly_kernel(const PolyArgs a) {
+__global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_kernel(
+    const PolyArgs a) {
     using C = Cfg<TR, MY, MX, TAX, RB, CB, WM, WN, KS>;
     using S = typename TR::storage;
     constexpr int VEC = C::VEC, KC = C::KC, RSA = C::RSA, BN = C::BN, T = C::T;
@@ -1030,13 +1033,14 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
     a->WY = in.TAY + (int)p.mH - 1 + a->spready;
     a->WX = in.TAX + (int)p.mW - 1 + a->spreadx;
     {
-        // Rows a multiple of 8 bytes long start 8-byte aligned (x itself is
+        // Rows a multiple of 4 bytes long start dword aligned (x itself is
         // 16-byte aligned), so a window start at a multiple of NP positions
-        // makes every x load aligned.  Tile starts are multiples of 16, so
-        // the shift is the same for every tile.
+        // makes every x load dword aligned (8-byte aligned when rows are a
+        // multiple of 8 bytes).  Tile starts are multiples of 16, so the
+        // shift is the same for every tile.
         const int es = p.dtype == CTCONV_F32 ? 4 : 2, np = 8 / es;
         const int w0 = a->dminx - ((int)p.mW - 1);
-        a->xofs = (p.W * es) % 8 == 0 ? ((w0 % np) + np) % np : 0;
+        a->xofs = (p.W * es) % 4 == 0 ? ((w0 % np) + np) % np : 0;
     }
     a->TCO = (int)TCO;
     a->PT = (int)PT;
