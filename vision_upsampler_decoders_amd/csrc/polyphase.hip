@@ -220,10 +220,9 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     // ---- x staging descriptors: item = (window row, NP positions, VEC channels)
     // Each channel of an item is one 8-byte global load (NP positions); the
     // VEC x NP block is transposed in registers into NP LDS rows of VEC
-    // channels.  Channel group fastest across lanes: the LDS rows written by
-    // one store instruction are NP apart, which maps 16 lanes onto 16 distinct
-    // 16-byte bank groups, and the lanes sharing a channel group still read a
-    // run that is contiguous along the spatial axis.
+    // channels.  Positions fastest across lanes: one load instruction of a
+    // wave reads a contiguous run of one channel plane (whole cache lines),
+    // which keeps the vector L1 to a few line accesses per instruction.
     constexpr int NP = C::NP;
     const int64_t HW = a.H * a.W;
     const int ngx = WXP / NP;
@@ -258,10 +257,10 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
         xsh[it] = 0;
         xpm[it] = 0;
         if (qw < xper && q < xitems) {
-            const int g = q % NG;
-            const int r2 = q / NG;
-            const int gx = r2 % ngx;
-            const int wy = r2 / ngx;
+            const int gx = q % ngx;
+            const int r2 = q / ngx;
+            const int wy = r2 % a.WY;
+            const int g = r2 / a.WY;
             const int iy = wy0 + wy;
             const bool rowok = iy >= 0 && iy < a.H;
             const int p0 = wx0 + gx * NP;
