@@ -92,12 +92,13 @@ ctconv_status ctconv_output_shape(int ndim, const int64_t* in_spatial, const int
 
 /*
  * Size in bytes of the packed weight that ctconv_prepack writes (host only).
- * The packed layout is phase-major: [P][C_out][T][C_in_pad] where
+ * The packed layout is phase-major, in blocks of 32 input channels:
+ * [P][C_in_pad / 32][C_out][T][32] where
  *   P = prod_d s_d output phases (phase (jy, jx) at jy*s_x + jx),
  *   T = prod_d ceil(k_d / s_d) taps per phase (tap (ry, rx) at ry*m_x + rx),
  *   C_in_pad = C_in rounded up to a multiple of 32,
- * holding w[ci, co, s_y*ry + jy, s_x*rx + jx], and zero where a tap index
- * reaches past the kernel or ci >= C_in.
+ * holding w[ci, co, s_y*ry + jy, s_x*rx + jx] for ci = 32*block + index,
+ * and zero where a tap index reaches past the kernel or ci >= C_in.
  */
 ctconv_status ctconv_packed_bytes(int ndim, int64_t C_in, int64_t C_out, const int64_t* kernel,
                                   const int64_t* stride, ctconv_dtype dtype, size_t* bytes);

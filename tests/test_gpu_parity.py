@@ -50,7 +50,7 @@ def _rand(shape, seed, dt, lo=-1.0, hi=1.0):
 
 
 def _pack_ref(w, s):
-    """packed[j][co][r][ci] = w[ci, co, sy*ry + jy, sx*rx + jx], zero padded."""
+    """packed[j][cb][co][r][cc] = w[32*cb + cc, co, sy*ry + jy, sx*rx + jx], zero padded."""
     C_in, C_out = w.shape[:2]
     k = w.shape[2:]
     if len(k) == 1:
@@ -69,7 +69,10 @@ def _pack_ref(w, s):
                     ty, tx = sH * ry + jy, sW * rx + jx
                     if ty < kH and tx < kW:
                         out[jy * sW + jx, :, ry * mW + rx, :C_in] = w[:, :, ty, tx].T
-    return out.reshape(-1)
+    # [j][co][r][ci] -> [j][ci // 32][co][r][ci % 32]
+    P, T = out.shape[0], out.shape[2]
+    out = out.reshape(P, C_out, T, Cp // 32, 32).transpose(0, 3, 1, 2, 4)
+    return np.ascontiguousarray(out).reshape(-1)
 
 
 @pytest.mark.parametrize("C_in,C_out,k,s,dt", [

@@ -52,12 +52,15 @@ __global__ __launch_bounds__(256) void gather_kernel(
 #pragma unroll
         for (int c = 0; c < kCoT; ++c) acc[c] = 0.f;
 
-        int64_t wrow[kCoT];  // packed row stride per output channel (clamped to C_out-1)
+        // packed layout [j][ci / 32][co][r][ci % 32]: per output channel the
+        // offset of its rows inside a 32-channel block (clamped to C_out-1)
+        int64_t wrow[kCoT];
 #pragma unroll
         for (int c = 0; c < kCoT; ++c) {
             const int64_t co = co0 + c < C_out ? co0 + c : C_out - 1;
-            wrow[c] = co * T * C_in_pad;
+            wrow[c] = co * T * kCinAlign;
         }
+        const int64_t blk = C_out * T * kCinAlign;  // one 32-channel block of a phase
 
         for (int64_t ty = 0; ty < kH; ++ty) {
             const int64_t ny = oy + pH - ty * dH;
@@ -71,14 +74,17 @@ __global__ __launch_bounds__(256) void gather_kernel(
                 if (ix >= W) continue;
                 const int64_t j = (ty % sH) * sW + (tx % sW);
                 const int64_t r = (ty / sH) * mW + (tx / sW);
-                const typename TR::storage* wp = pw + (j * C_out * T + r) * C_in_pad;
+                const typename TR::storage* wj =
+                    pw + j * (C_in_pad / kCinAlign) * blk + r * kCinAlign;
                 const typename TR::storage* xp = x + ((n * C_in) * H + iy) * W + ix;
                 const int64_t HW = H * W;
                 for (int64_t ci = 0; ci < C_in; ++ci) {
                     const float xv = TR::to_f32(xp[ci * HW]);
+                    const typename TR::storage* wp =
+                        wj + (ci / kCinAlign) * blk + (ci % kCinAlign);
 #pragma unroll
                     for (int c = 0; c < kCoT; ++c)
-                        acc[c] = fmaf(xv, TR::to_f32(wp[wrow[c] + ci]), acc[c]);
+                        acc[c] = fmaf(xv, TR::to_f32(wp[wrow[c]]), acc[c]);
                 }
             }
         }

@@ -326,8 +326,10 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
             if (pb < a.PT && b < a.P && co < a.C_out) {
                 const int by = b / a.sx, bx = b % a.sx;
                 const int j = ((by + a.py) % a.sy) * a.sx + (bx + a.px) % a.sx;
-                boff[it] = (uint32_t)(((((int64_t)j * a.C_out + co) * T + r) * a.C_in_pad +
-                                       piece * VEC) * C::ES);
+                // packed layout [j][ci / 32][co][r][ci % 32]: row (co, r) of
+                // phase j in channel block 0 (the chunk adds its block)
+                boff[it] = (uint32_t)((((int64_t)j * (a.C_in_pad / kCinAlign) * a.C_out + co) * T +
+                                       r) * kCinAlign + piece * VEC) * C::ES;
             }
             blds[it] = (r * BN + tc) * RSA + piece * VEC;
         }
@@ -387,10 +389,14 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                                                                     (cbase + e) * ch_bytes, 0));
                 }
             }
+        // the chunk's channel block (a column tile's rows of one block are
+        // contiguous) and its offset inside the block
+        const uint32_t bchunk = uniform(((cbase / kCinAlign) * (uint32_t)(a.C_out * T) * kCinAlign +
+                                         cbase % kCinAlign) * C::ES);
 #pragma unroll
         for (int it = 0; it < C::BITEMS; ++it)
             br[it] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(brs, boff[it], cbase * C::ES, 0));
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(brs, boff[it], bchunk, 0));
     };
     // `inside`: true_type when the caller knows that no item of the wave needs
     // realignment or masks, false_type to decide from wave_inside at run time

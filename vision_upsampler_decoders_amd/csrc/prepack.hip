@@ -4,11 +4,12 @@
 // kernel into s phases of m taps each, tap r of phase j being w[s*r + j]
 // (ExecuTorch PR #25037, Summary formula, with r = m - 1 - u); the phases are
 // ordered phase-major, as the page's depth-to-space expects.  This kernel
-// writes that split once per weight so both compute kernels read contiguous
-// input-channel runs:
+// writes that split once per weight, in blocks of 32 input channels, so that
+// the weights a column tile needs for one block of input channels (all its
+// output channels and taps) are one contiguous run:
 //
-//   packed[j][co][r][ci] = w[ci, co, sH*rH + jH, sW*rW + jW]
-//   j = jH*sW + jW,  r = rH*mW + rW,  ci < C_in_pad (multiple of 32),
+//   packed[j][cb][co][r][cc] = w[ci, co, sH*rH + jH, sW*rW + jW],  ci = 32*cb + cc
+//   j = jH*sW + jW,  r = rH*mW + rW,  cb < C_in_pad / 32,
 //
 // zero where a tap index reaches past the kernel (k not a multiple of s) or
 // ci >= C_in.  A pure copy of bit patterns: no arithmetic.
@@ -26,12 +27,15 @@ __global__ __launch_bounds__(256) void prepack_kernel(const S* __restrict__ w,
                                                       int64_t mW) {
     for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t ci = idx % C_in_pad;
-        int64_t rest = idx / C_in_pad;
+        const int64_t cc = idx % kCinAlign;
+        int64_t rest = idx / kCinAlign;
         const int64_t r = rest % T;
         rest /= T;
         const int64_t co = rest % C_out;
-        const int64_t j = rest / C_out;
+        rest /= C_out;
+        const int64_t cb = rest % (C_in_pad / kCinAlign);
+        const int64_t j = rest / (C_in_pad / kCinAlign);
+        const int64_t ci = cb * kCinAlign + cc;
         const int64_t ty = sH * (r / mW) + j / sW;
         const int64_t tx = sW * (r % mW) + j % sW;
         S v = S(0);
