@@ -12,16 +12,20 @@
  * #20849 ("[ExecuTorch][WebGPU] Add optimized conv2d op", Implementation).
  *
  * Two routes compute it:
- *  - polyphase: when every kernel size is a multiple of its stride (k = m*s),
- *    dilation is 1 and output_padding is 0, the operation is one stride-1
- *    m-tap convolution producing every output phase, followed by a phase
- *    interleave (depth-to-space) and a padding slice -- ExecuTorch PR #25037
- *    ("[XNNPACK] Lower dense transposed convs as one polyphase conv + depth to
- *    space", Summary formula).  Here it runs as an implicit GEMM on the MFMA
- *    matrix cores with the interleave, slice and bias fused into its epilogue.
- *    Its kernels cover m <= 4 (1-D) or m <= 2 per dimension (2-D) and input
- *    rows of at least 8 bytes (W >= 4 for bf16/fp16, W >= 2 for fp32).
- *  - gather: every other shape, one output at a time from the tap condition.
+ *  - polyphase: when every kernel size is a multiple of its stride (k = m*s)
+ *    the operation is one stride-1 m-tap convolution producing every output
+ *    phase, followed by a phase interleave (depth-to-space) and a padding
+ *    slice -- ExecuTorch PR #25037 ("[XNNPACK] Lower dense transposed convs
+ *    as one polyphase conv + depth to space", Summary formula).  The same
+ *    holds for any k with m = ceil(k / s) taps per phase, the taps past k
+ *    being zero in the packed weight, and output_padding only lengthens the
+ *    output, so this route takes every shape with dilation 1.  It runs as an
+ *    implicit GEMM on the MFMA matrix cores with the interleave, slice and
+ *    bias fused into its epilogue, for m <= 4 (1-D) or m <= 2 per dimension
+ *    (2-D) and input rows of at least 8 bytes (W >= 4 for bf16/fp16, W >= 2
+ *    for fp32).
+ *  - gather: every other shape (dilation, more taps, shorter rows), one
+ *    output at a time from the tap condition.
  *
  * Layouts.  x [N, C_in, L] or [N, C_in, H, W]; y [N, C_out, L_out] or
  * [N, C_out, H_out, W_out]; bias [C_out]; all dense row-major (contiguous).

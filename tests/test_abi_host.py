@@ -5,8 +5,8 @@
   invalid parameters;
 * ctconv_packed_bytes follows the documented packed layout size;
 * argument validation returns the documented status before any launch;
-* routing: shapes with k = m*s, dilation 1 and no output_padding take the
-  polyphase kernel, the rest the gather kernel.
+* routing: shapes with dilation 1 take the polyphase kernel (within its
+  compiled tap counts and row widths), the rest the gather kernel.
 """
 
 import ctypes
@@ -134,9 +134,9 @@ def test_forward_validation_before_launch(lib):
     assert _fwd(lib, y=0x3008) == 5
     assert _fwd(lib, b=0x4004) == 5
     # polyphase forced on a shape outside the polyphase form
-    assert _fwd(lib, k=3, route=1) == 3
-    assert _fwd(lib, op=1, route=1) == 3
     assert _fwd(lib, d=2, k=4, route=1) == 3
+    assert _fwd(lib, k=20, s=4, p=2, route=1) == 3   # 5 taps per phase
+    assert _fwd(lib, sp=(3,), dt=1, route=1) == 3     # rows shorter than 8 bytes
     assert lib.ctconv_elu(None, 0x1000, 4, 0, None) == 1
     assert lib.ctconv_elu(0x1000, 0x2000, -1, 0, None) == 2
     assert lib.ctconv_elu(0x1000, 0x2000, 4, 5, None) == 4
@@ -149,7 +149,7 @@ def test_forward_with_N_zero_enqueues_nothing(lib):
 
 @pytest.mark.parametrize("name,route", [
     ("upsampler1d_small", 1), ("vocoder_stack", 1), ("istft", 1), ("upsampler2d", 1),
-    ("gather2d", 2), ("gather2d_dil2", 2),
+    ("gather2d", 1), ("gather2d_dil2", 2),
 ])
 def test_routes_of_workloads(lib, name, route):
     from synth import inputs as I
@@ -166,11 +166,12 @@ def test_routes_of_workloads(lib, name, route):
 
 
 @pytest.mark.parametrize("k,s,p,op,d,route", [
-    (8, 4, 2, 0, 1, 1), (6, 3, 0, 0, 1, 1), (4, 1, 1, 0, 1, 1), (3, 2, 1, 0, 1, 2),
-    (8, 4, 2, 1, 1, 2), (8, 4, 2, 0, 2, 2), (16, 4, 2, 0, 1, 1), (20, 4, 2, 0, 1, 2),
+    (8, 4, 2, 0, 1, 1), (6, 3, 0, 0, 1, 1), (4, 1, 1, 0, 1, 1), (3, 2, 1, 0, 1, 1),
+    (8, 4, 2, 1, 1, 1), (8, 4, 2, 0, 2, 2), (16, 4, 2, 0, 1, 1), (20, 4, 2, 0, 1, 2),
+    (7, 3, 2, 2, 1, 1), (13, 4, 1, 0, 1, 1), (17, 4, 1, 0, 1, 2),
 ])
 def test_route_rule(lib, k, s, p, op, d, route):
-    # polyphase iff k % s == 0, d == 1, op == 0 (and m = k/s within the compiled taps)
+    # polyphase iff d == 1 and m = ceil(k / s) within the compiled taps
     assert C.ctconv_query_route(2, 16, 16, (50,), k, s, p, op, d, 1) == route
 
 

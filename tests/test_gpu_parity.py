@@ -133,6 +133,12 @@ FULL_CASES = [
     # channels, and a 2-D plane of odd size (odd channels 2 bytes off)
     ("odd_len_bf16", "bf16", 2, 40, 24, (301,), (8,), (4,), (2,), (0,), (1,), True),
     ("odd_plane_2d_bf16", "bf16", 2, 36, 16, (5, 7), (4, 4), (2, 2), (1, 1), (0, 0), (1, 1), True),
+    # k not a multiple of s and output_padding on the polyphase route (zero
+    # taps past k; longer output)
+    ("k7_s3_op1_bf16", "bf16", 2, 48, 24, (200,), (7,), (3,), (2,), (1,), (1,), True),
+    ("k5_s4_op3_f16", "f16", 2, 40, 20, (130,), (5,), (4,), (1,), (3,), (1,), False),
+    ("k3_s2_op1_2d_f32", "f32", 2, 24, 12, (13, 17), (3, 3), (2, 2), (0, 1), (1, 1), (1, 1), True),
+    ("k3x4_s2x3_2d_bf16", "bf16", 1, 40, 24, (12, 15), (3, 4), (2, 3), (1, 0), (0, 2), (1, 1), True),
 ]
 
 

@@ -119,9 +119,9 @@ ctconv_status build_problem(int64_t N, int64_t C_in, int64_t C_out, int ndim,
 }
 
 bool polyphase_eligible(const Problem& p) {
-    // k a multiple of s in every dimension, no dilation, no output_padding.
-    return p.kH % p.sH == 0 && p.kW % p.sW == 0 && p.dH == 1 && p.dW == 1 && p.opH == 0 &&
-           p.opW == 0;
+    // No dilation.  Any k: with m = ceil(k / s) taps per phase the packed
+    // weight's taps past k are zero; output_padding only lengthens the output.
+    return p.dH == 1 && p.dW == 1;
 }
 
 ctconv_route choose_route(const Problem& p) {

@@ -1,12 +1,15 @@
 // Polyphase transposed convolution as an implicit GEMM on the gfx950 MFMA
 // matrix cores.
 //
-// Method.  For k = m*s (per dimension), d = 1 and output_padding 0, a
-// transposed convolution is one stride-1 convolution with m taps that yields
-// every output phase, followed by an interleave of the phases and a slice of
-// the padding (ExecuTorch PR #25037, "[XNNPACK] Lower dense transposed convs
-// as one polyphase conv + depth to space", Summary formula
-// y[s*q + j] = sum_{u<m} x[q + u - (m-1)] * w[s*(m-1-u) + j]).
+// Method.  For k = m*s (per dimension) and d = 1, a transposed convolution is
+// one stride-1 convolution with m taps that yields every output phase,
+// followed by an interleave of the phases and a slice of the padding
+// (ExecuTorch PR #25037, "[XNNPACK] Lower dense transposed convs as one
+// polyphase conv + depth to space", Summary formula
+// y[s*q + j] = sum_{u<m} x[q + u - (m-1)] * w[s*(m-1-u) + j]).  The identity
+// below holds for any k with m = ceil(k / s) when the taps s*r + j >= k are
+// zero (the packed weight is zero there), and output_padding only extends the
+// range of output rows, so every shape with d = 1 takes this kernel.
 //
 // Output-aligned phases.  Writing each output index as o = s*a + b (b the
 // output phase) and j_b = (b + p) mod s, delta_b = floor((b + p) / s), the
@@ -961,7 +964,7 @@ constexpr int64_t kInt32Max = 2147483647;
 
 // Fill PolyArgs for problem p; false when no kernel instance covers it.
 bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
-    if (p.kH % p.sH || p.kW % p.sW || p.dH != 1 || p.dW != 1 || p.opH || p.opW) return false;
+    if (p.dH != 1 || p.dW != 1) return false;
     if (p.H == 0 || p.W == 0 || p.N == 0) return false;
     // every staged x load covers 8 bytes of one input row
     if (p.W * (p.dtype == CTCONV_F32 ? 4 : 2) < 8) return false;
