@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="vocoder_stack")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-elu", action="store_true",
+                    help="run the ELU between layers as its own pass instead of fusing it "
+                         "into the producing layer's epilogue")
     ap.add_argument("--cpu-items", type=int, default=2,
                     help="batch items of the workload in the oracle's timed sample")
     ap.add_argument("--cpu-frames", type=int, default=0,
@@ -169,7 +172,8 @@ def main():
         b = I.gen_bias(wl, li)
         biases.append(None if b is None else dev(b))
         outs.append(torch.empty((wl.N, L.C_out) + osp, dtype=tdt, device="cuda"))
-        elus.append(torch.empty_like(outs[-1]) if (wl.elu_between and li + 1 < len(geo)) else None)
+        elus.append(torch.empty_like(outs[-1])
+                    if (args.separate_elu and wl.elu_between and li + 1 < len(geo)) else None)
         del w
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
@@ -178,8 +182,11 @@ def main():
 
     n_layers = len(geo)
     # arguments marshalled once per layer: each launch is one foreign call
+    fuse = wl.elu_between and not args.separate_elu
     convs = [C.Conv(wl.N, L.C_in, L.C_out, sp, L.kernel, L.stride, L.padding, L.output_padding,
-                    L.dilation, dcode) for (L, sp, osp, _, _) in geo]
+                    L.dilation, dcode,
+                    act=C.ACT_ELU if (fuse and li + 1 < len(geo)) else C.ACT_NONE)
+             for li, (L, sp, osp, _, _) in enumerate(geo)]
     ptrs = []
     cur_ptr = x.data_ptr()
     for li in range(n_layers):
@@ -288,6 +295,8 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {"workload": wl.name, "description": wl.note, "N": wl.N,
                    "in_spatial": list(wl.in_spatial), "parallelism": "none (1 GPU)",
+                   "elu": ("fused into the producing layer" if fuse else
+                           "separate pass" if wl.elu_between else "none"),
                    "layers": [{"C_in": g[0].C_in, "C_out": g[0].C_out, "k": list(g[0].kernel),
                                "s": list(g[0].stride), "p": list(g[0].padding),
                                "op": list(g[0].output_padding), "d": list(g[0].dilation)}

@@ -75,6 +75,12 @@ typedef enum {
     CTCONV_ROUTE_GATHER = 2     /* force the gather kernel (valid for every shape) */
 } ctconv_route;
 
+/* Activation applied to every output (after the bias, before the one rounding). */
+typedef enum {
+    CTCONV_ACT_NONE = 0,
+    CTCONV_ACT_ELU = 1 /* x > 0 ? x : exp(x) - 1 (alpha = 1) */
+} ctconv_activation;
+
 /* Version of this ABI (CTCONV_ABI_VERSION). */
 int ctconv_abi_version(void);
 
@@ -148,6 +154,25 @@ ctconv_status ctconv_forward_route(const void* x, const void* packed_w, const vo
                                    const int64_t* stride, const int64_t* padding,
                                    const int64_t* output_padding, const int64_t* dilation,
                                    ctconv_dtype dtype, ctconv_route route, void* stream);
+
+/*
+ * ctconv_forward_route with a pointwise activation fused into the epilogue:
+ * y = act(conv + bias), computed in fp32 and rounded once to the output
+ * type.  The activation is applied where the transposed convolution writes
+ * its output instead of in a separate pass that reads and writes y again
+ * (ExecuTorch PR #25037 runs its polyphase rewrite before FuseActivationPass
+ * for the same reason; its Test plan has two deconvolutions with an ELU
+ * between them).  Outputs no tap reaches get act(bias) (or act(0)).
+ * act outside ctconv_activation returns CTCONV_ERR_PARAM; everything else
+ * as in ctconv_forward_route.
+ */
+ctconv_status ctconv_forward_act(const void* x, const void* packed_w, const void* bias, void* y,
+                                 int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                                 const int64_t* in_spatial, const int64_t* kernel,
+                                 const int64_t* stride, const int64_t* padding,
+                                 const int64_t* output_padding, const int64_t* dilation,
+                                 ctconv_dtype dtype, ctconv_activation act, ctconv_route route,
+                                 void* stream);
 
 /*
  * Which kernel ctconv_forward would run for these arguments (host only):

@@ -137,6 +137,11 @@ def test_forward_validation_before_launch(lib):
     assert _fwd(lib, d=2, k=4, route=1) == 3
     assert _fwd(lib, k=20, s=4, p=2, route=1) == 3   # 5 taps per phase
     assert _fwd(lib, sp=(3,), dt=1, route=1) == 3     # rows shorter than 8 bytes
+    # fused activation: an unknown activation is rejected
+    nd = 1
+    arr = lambda v: (ctypes.c_int64 * nd)(*C.per_dim(v, nd))  # noqa: E731
+    assert lib.ctconv_forward_act(0x1000, 0x2000, None, 0x3000, 1, 4, 4, nd, arr((8,)), arr(4),
+                                  arr(2), arr(1), arr(0), arr(1), 0, 7, 0, None) == 3
     assert lib.ctconv_elu(None, 0x1000, 4, 0, None) == 1
     assert lib.ctconv_elu(0x1000, 0x2000, -1, 0, None) == 2
     assert lib.ctconv_elu(0x1000, 0x2000, 4, 5, None) == 4

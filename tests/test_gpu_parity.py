@@ -252,6 +252,115 @@ def test_vocoder_stack_end_to_end_short(cc):
     assert err <= 1e-2
 
 
+# ---------------------------------------------------------------------------
+# fused activation: y = ELU(conv + bias), one rounding
+# ---------------------------------------------------------------------------
+
+ACT_CASES = [
+    # name, dt, N, C_in, C_out, spatial, k, s, p, op, d, bias
+    ("act_voc_l2", "bf16", 2, 256, 128, (300,), (10,), (5,), (3,), (0,), (1,), True),
+    ("act_voc_l1", "bf16", 2, 512, 64, (120,), (16,), (8,), (4,), (0,), (1,), False),
+    ("act_f32_2d", "f32", 2, 24, 20, (13, 11), (4, 4), (2, 2), (1, 1), (0, 0), (1, 1), True),
+    ("act_f16_gather_dil", "f16", 1, 40, 12, (37,), (5,), (3,), (2,), (1,), (2,), True),
+]
+
+
+@pytest.mark.parametrize("case", ACT_CASES, ids=[c[0] for c in ACT_CASES])
+@pytest.mark.parametrize("route", [0, 2], ids=["auto", "gather"])
+def test_fused_elu_parity(cc, case, route):
+    import torch
+
+    from oracle import conv_transpose, elu as oelu, rel_l2
+
+    name, dt, N, C_in, C_out, sp, k, s, p, op, d, has_b = case
+    say(f"fused elu {name} route={route}")
+    seed = 700 + len(name)
+    x64 = I.normal(seed, (N, C_in) + sp, 1.0, dt)
+    w64 = I.normal(seed + 1, (C_in, C_out) + k, (C_in * np.prod(k)) ** -0.5, dt)
+    b64 = _rand((C_out,), seed + 2, dt, -0.1, 0.1) if has_b else None
+    pw = cc.prepack(to_dev(w64, dt), s)
+    y = cc.forward(to_dev(x64, dt), pw, None if b64 is None else to_dev(b64, dt), C_out, k, s, p,
+                   op, d, route=route, act=cc.ACT_ELU)
+    torch.cuda.synchronize()
+    ref = oelu(conv_transpose(x64, w64, b64, s, p, op, d))
+    err = rel_l2(to_host(y), ref)
+    say(f"  rel_l2 = {err:.3e}")
+    assert err <= TOL[dt], err
+
+
+@pytest.mark.parametrize("case", ACT_CASES, ids=[c[0] for c in ACT_CASES])
+@pytest.mark.parametrize("route", [0, 2], ids=["auto", "gather"])
+def test_fused_elu_matches_forward_then_elu_bitwise(cc, case, route):
+    """The fused activation is the same fp32 function that the standalone ELU
+    pass applies.  For fp32 storage the unfused pair rounds nothing in
+    between, so the two agree bit for bit.  For 16-bit storage the unfused
+    pair rounds before the ELU as well as after.  For v < 0 the slope e^v of
+    the ELU times |v| is at most |e^v - 1| (u e^-u <= 1 - e^-u), so the first
+    rounding, relative error 2^-9 (bf16) or 2^-12 (fp16) of v, moves the
+    result by at most that relative amount of it, one unit in its last place;
+    with the two final roundings the results differ by at most two units."""
+    import torch
+
+    name, dt, N, C_in, C_out, sp, k, s, p, op, d, has_b = case
+    say(f"fused vs unfused elu {name} route={route}")
+    seed = 900 + len(name)
+    x = to_dev(I.normal(seed, (N, C_in) + sp, 1.0, dt), dt)
+    w = to_dev(I.normal(seed + 1, (C_in, C_out) + k, (C_in * np.prod(k)) ** -0.5, dt), dt)
+    b = to_dev(_rand((C_out,), seed + 2, dt, -0.1, 0.1), dt) if has_b else None
+    pw = cc.prepack(w, s)
+    fused = cc.forward(x, pw, b, C_out, k, s, p, op, d, route=route, act=cc.ACT_ELU)
+    plain = cc.forward(x, pw, b, C_out, k, s, p, op, d, route=route)
+    sep = cc.elu(plain)
+    torch.cuda.synchronize()
+    if dt == "f32":
+        assert torch.equal(fused, sep)
+    else:
+        bits = lambda t: t.view(torch.int16).to(torch.int32)
+        assert int((bits(fused) - bits(sep)).abs().max()) <= 2
+
+
+def test_fused_elu_empty_input_fills_act_of_bias(cc):
+    import torch
+
+    from oracle import elu as oelu
+
+    b64 = _rand((6,), 31, "f32", -1.0, 1.0)
+    x = torch.empty((2, 4, 0), dtype=torch.float32, device="cuda")
+    w64 = _rand((4, 6, 8), 32, "f32")
+    pw = cc.prepack(to_dev(w64, "f32"), (4,))
+    y = cc.forward(x, pw, to_dev(b64, "f32"), 6, (8,), (4,), (0,), act=cc.ACT_ELU)
+    torch.cuda.synchronize()
+    got = to_host(y)
+    assert got.shape == (2, 6, 4)
+    ref = np.broadcast_to(oelu(b64.astype(np.float32).astype(np.float64))[None, :, None], got.shape)
+    assert np.allclose(got, ref, rtol=1e-6, atol=1e-7)
+
+
+def test_vocoder_stack_fused_elu_full_size(cc):
+    """Layers 0 and 1 of the stack with the ELU fused, at full size, sampled:
+    the oracle (conv, then ELU in float64) fed the GPU's own layer input."""
+    import torch
+
+    from oracle import conv_transpose_points, elu as oelu, rel_l2
+
+    wl = I.workload("vocoder_stack")
+    x = to_dev(I.gen_x(wl), wl.dtype)
+    for li, L in enumerate(wl.layers[:2]):
+        w64 = I.gen_w(wl, li)
+        pw = cc.prepack(to_dev(w64, wl.dtype), L.stride)
+        y = cc.forward(x, pw, None, L.C_out, L.kernel, L.stride, L.padding, act=cc.ACT_ELU)
+        torch.cuda.synchronize()
+        xin64 = to_host(x)
+        idx = sample_indices(tuple(y.shape), 1500, 950 + li, ())
+        it = torch.from_numpy(idx).to(y.device)
+        got = y[it[:, 0], it[:, 1], it[:, 3]].to(torch.float64).cpu().numpy()
+        ref = oelu(conv_transpose_points(xin64, w64, None, idx, L.stride, L.padding, 0, 1))
+        err = rel_l2(got, ref)
+        say(f"  fused-elu layer {li}: sampled rel_l2 = {err:.3e}")
+        assert err <= TOL[wl.dtype], err
+        x = y
+
+
 def test_istft_full_size(cc):
     """Whole output against the independent radix-2 irfft + overlap-add oracle."""
     import torch

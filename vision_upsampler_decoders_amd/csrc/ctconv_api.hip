@@ -210,19 +210,22 @@ ctconv_status ctconv_query_route(int64_t N, int64_t C_in, int64_t C_out, int ndi
     return CTCONV_OK;
 }
 
-ctconv_status ctconv_forward_route(const void* x, const void* packed_w, const void* bias, void* y,
-                                   int64_t N, int64_t C_in, int64_t C_out, int ndim,
-                                   const int64_t* in_spatial, const int64_t* kernel,
-                                   const int64_t* stride, const int64_t* padding,
-                                   const int64_t* output_padding, const int64_t* dilation,
-                                   ctconv_dtype dtype, ctconv_route route, void* stream) {
+ctconv_status ctconv_forward_act(const void* x, const void* packed_w, const void* bias, void* y,
+                                 int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                                 const int64_t* in_spatial, const int64_t* kernel,
+                                 const int64_t* stride, const int64_t* padding,
+                                 const int64_t* output_padding, const int64_t* dilation,
+                                 ctconv_dtype dtype, ctconv_activation act, ctconv_route route,
+                                 void* stream) {
     if (route != CTCONV_ROUTE_AUTO && route != CTCONV_ROUTE_POLYPHASE &&
         route != CTCONV_ROUTE_GATHER)
         return CTCONV_ERR_PARAM;
+    if (act != CTCONV_ACT_NONE && act != CTCONV_ACT_ELU) return CTCONV_ERR_PARAM;
     Problem p;
     const ctconv_status st = build_problem(N, C_in, C_out, ndim, in_spatial, kernel, stride,
                                            padding, output_padding, dilation, dtype, &p);
     if (st != CTCONV_OK) return st;
+    p.act = (int)act;
     // x may be NULL when it holds no element, y when N = 0 (empty tensors)
     const bool x_empty = p.N == 0 || p.H == 0 || p.W == 0;
     if (!packed_w || (!x && !x_empty) || (!y && p.N != 0)) return CTCONV_ERR_NULL;
@@ -238,6 +241,17 @@ ctconv_status ctconv_forward_route(const void* x, const void* packed_w, const vo
     if (route == CTCONV_ROUTE_AUTO) route = choose_route(p);
     if (route == CTCONV_ROUTE_POLYPHASE) return to_status(launch_polyphase(p, x, packed_w, bias, y, s));
     return to_status(launch_gather(p, x, packed_w, bias, y, s));
+}
+
+ctconv_status ctconv_forward_route(const void* x, const void* packed_w, const void* bias, void* y,
+                                   int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                                   const int64_t* in_spatial, const int64_t* kernel,
+                                   const int64_t* stride, const int64_t* padding,
+                                   const int64_t* output_padding, const int64_t* dilation,
+                                   ctconv_dtype dtype, ctconv_route route, void* stream) {
+    return ctconv_forward_act(x, packed_w, bias, y, N, C_in, C_out, ndim, in_spatial, kernel,
+                              stride, padding, output_padding, dilation, dtype, CTCONV_ACT_NONE,
+                              route, stream);
 }
 
 ctconv_status ctconv_forward(const void* x, const void* packed_w, const void* bias, void* y,

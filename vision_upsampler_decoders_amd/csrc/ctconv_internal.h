@@ -59,7 +59,38 @@ struct Problem {
     int64_t P, T;     // phases sH*sW, taps mH*mW
     int64_t C_in_pad; // C_in rounded up to 32
     ctconv_dtype dtype;
+    int act;          // ctconv_activation applied to every output before rounding
 };
+
+// ELU with alpha = 1, computed in fp32 and rounded once to the storage type
+// (the fused epilogues and the standalone ELU kernel share it, so a fused
+// forward and a forward followed by the ELU pass agree bit for bit).  For
+// v <= 0 it needs e^v - 1, branch free:
+//  - fp32 storage: above -1/2 the Taylor series of e^t - 1 through t^8
+//    (truncation below 2e-8 relative there), else 2^(t log2 e) - 1 from the
+//    hardware exp2, whose cancellation error is at most ~2.5 ulp at -1/2 and
+//    shrinks below it;
+//  - 16-bit storage: 2^(t log2 e) - 1 everywhere; its absolute error (about
+//    1e-7) stays below half an ulp of the bf16/fp16 result down to |v| ~ 1e-4.
+// A NaN passes through.
+template <class TR>
+__device__ inline float elu_act(float v) {
+    const float t = v > 0.f ? 0.f : v;
+    const float e = __builtin_amdgcn_exp2f(t * 1.44269504088896341f) - 1.f;
+    float m = e;
+    if constexpr (sizeof(typename TR::storage) == 4) {
+        float p = 1.f / 40320.f;
+        p = fmaf(p, t, 1.f / 5040.f);
+        p = fmaf(p, t, 1.f / 720.f);
+        p = fmaf(p, t, 1.f / 120.f);
+        p = fmaf(p, t, 1.f / 24.f);
+        p = fmaf(p, t, 1.f / 6.f);
+        p = fmaf(p, t, 0.5f);
+        p = fmaf(p, t, 1.f) * t;
+        m = t > -0.5f ? p : e;
+    }
+    return v > 0.f ? v : m;
+}
 
 constexpr int64_t kCinAlign = 32;
 
@@ -90,6 +121,7 @@ struct PolyArgs {
     int atomic_out;        // 1: accumulate with fp32 atomics into a pre-filled y
     int xcd_remap;         // 1: gridDim.x is a multiple of 8, remap for L2 locality
     uint32_t pw_bytes;     // size of the packed weight (below 2^32)
+    int act;               // ctconv_activation of the epilogue
 };
 
 // Launchers (each returns hipGetLastError() of its launch).

@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void gather_kernel(
     const typename TR::storage* __restrict__ bias, typename TR::storage* __restrict__ y,
     int64_t total, int64_t C_in, int64_t C_out, int64_t C_in_pad, int64_t H, int64_t W,
     int64_t Ho, int64_t Wo, int64_t Wq, int64_t n_cot, int64_t kH, int64_t kW, int64_t sH,
-    int64_t sW, int64_t pH, int64_t pW, int64_t dH, int64_t dW, int64_t mW, int64_t T) {
+    int64_t sW, int64_t pH, int64_t pW, int64_t dH, int64_t dW, int64_t mW, int64_t T, int act) {
     for (int64_t id = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; id < total;
          id += (int64_t)gridDim.x * blockDim.x) {
         const int64_t ax = id % Wq;
@@ -93,7 +93,9 @@ __global__ __launch_bounds__(256) void gather_kernel(
             const int64_t co = co0 + c;
             if (co < C_out) {
                 const float b = bias ? TR::to_f32(bias[co]) : 0.f;
-                y[((n * C_out + co) * Ho + oy) * Wo + ox] = TR::from_f32(acc[c] + b);
+                float v = acc[c] + b;
+                if (act == CTCONV_ACT_ELU) v = elu_act<TR>(v);
+                y[((n * C_out + co) * Ho + oy) * Wo + ox] = TR::from_f32(v);
             }
         }
     }
@@ -112,7 +114,7 @@ hipError_t launch_gather_t(const Problem& p, const void* x, const void* pw, cons
     gather_kernel<TR><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(
         static_cast<const S*>(x), static_cast<const S*>(pw), static_cast<const S*>(bias),
         static_cast<S*>(y), total, p.C_in, p.C_out, p.C_in_pad, p.H, p.W, p.Ho, p.Wo, Wq, n_cot,
-        p.kH, p.kW, p.sH, p.sW, p.pH, p.pW, p.dH, p.dW, p.mW, p.T);
+        p.kH, p.kW, p.sH, p.sW, p.pH, p.pW, p.dH, p.dW, p.mW, p.T, p.act);
     return hipGetLastError();
 }
 

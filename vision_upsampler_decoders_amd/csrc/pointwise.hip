@@ -7,6 +7,8 @@
 // split-over-C_in launch accumulates into it.
 //
 // elu: y = x for x > 0, exp(x) - 1 otherwise (alpha = 1), in fp32, one rounding.
+// The fill applies the forward call's activation to what it writes, except
+// before a split-over-C_in accumulation (which never carries an activation).
 
 #include "ctconv_internal.h"
 
@@ -17,11 +19,13 @@ namespace {
 template <class TR>
 __global__ __launch_bounds__(256) void fill_kernel(const typename TR::storage* __restrict__ bias,
                                                    typename TR::storage* __restrict__ y,
-                                                   int64_t total, int64_t plane, int64_t C_out) {
+                                                   int64_t total, int64_t plane, int64_t C_out,
+                                                   int act) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * blockDim.x) {
         typename TR::storage v = TR::from_f32(0.f);
         if (bias) v = bias[(i / plane) % C_out];
+        if (act == CTCONV_ACT_ELU) v = TR::from_f32(elu_act<TR>(TR::to_f32(v)));
         y[i] = v;
     }
 }
@@ -31,8 +35,7 @@ __global__ __launch_bounds__(256) void elu_kernel(const typename TR::storage* x,
                                                   typename TR::storage* y, int64_t n) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x) {
-        const float v = TR::to_f32(x[i]);
-        y[i] = TR::from_f32(v > 0.f ? v : expm1f(v));
+        y[i] = TR::from_f32(elu_act<TR>(TR::to_f32(x[i])));
     }
 }
 
@@ -45,8 +48,7 @@ __global__ __launch_bounds__(256) void elu_kernel_v8(const uint4* x, uint4* y, i
         uint16_t* h = reinterpret_cast<uint16_t*>(&v);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float f = TR::to_f32(h[e]);
-            h[e] = TR::from_f32(f > 0.f ? f : expm1f(f));
+            h[e] = TR::from_f32(elu_act<TR>(TR::to_f32(h[e])));
         }
         y[i] = v;
     }
@@ -64,7 +66,7 @@ hipError_t fill_t(const Problem& p, const void* bias, void* y, hipStream_t s) {
     const int64_t plane = p.Ho * p.Wo;
     const int64_t total = p.N * p.C_out * plane;
     fill_kernel<TR><<<dim3((unsigned)grid_for(total)), dim3(256), 0, s>>>(
-        static_cast<const S*>(bias), static_cast<S*>(y), total, plane, p.C_out);
+        static_cast<const S*>(bias), static_cast<S*>(y), total, plane, p.C_out, p.act);
     return hipGetLastError();
 }
 

@@ -140,6 +140,19 @@ __device__ inline void transpose_block(const u32x2 (&in)[4], u32x4 (&out)[2]) {
     for (int p = 0; p < 2; ++p) out[p] = u32x4{in[0][p], in[1][p], in[2][p], in[3][p]};
 }
 
+// Two fp32 values rounded to the 16-bit storage type and packed into one
+// dword (low half first): one packed conversion instruction for bf16.
+template <class TR>
+__device__ inline uint32_t pack2(float f0, float f1) {
+    if constexpr (std::is_same_v<TR, TBF16>) {
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{f0, f1}, bf16x2));
+    } else {
+        return (uint32_t)TR::from_f32(f0) | ((uint32_t)TR::from_f32(f1) << 16);
+    }
+}
+
 template <class TR, int MY, int MX, int TAX, int RB, int CB, int WM, int WN, int KS>
 struct Cfg {
     using S = typename TR::storage;
@@ -713,101 +726,116 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     // hold consecutive output channels, so an unpadded power-of-two stride
     // would put all 16 of their staging writes in one LDS bank
     const int CSTR = R * SS + VEC;
-    // Column block cb holds 16 consecutive output channels of one phase when
-    // TCO is a multiple of 16 (every shape but the narrow and phase-subset
-    // ones): its phase, channel base and row offsets are wave-uniform, and
-    // block cb + TCO/16 holds the next phase of the same channels, i.e. the
-    // next output element of a row, so the two values go out as one 4-byte
-    // LDS write when both phases sit in the same output row.
-    auto stage_pairs = [&](auto step_tag) __attribute__((always_inline)) {
-        constexpr int STEP = decltype(step_tag)::value;  // TCO / 16 (0: no pairing)
-        const int T0 = wm * RB * 16;
+    // The output staging, compiled once without and once with the fused
+    // activation (applied in fp32 after the bias, before the one rounding).
+    auto stage_all = [&](auto act_tag) __attribute__((always_inline)) {
+        auto actf = [](float v) __attribute__((always_inline)) {
+            if constexpr (decltype(act_tag)::value) return elu_act<TR>(v);
+            else return v;
+        };
+        // Column block cb holds 16 consecutive output channels of one phase when
+        // TCO is a multiple of 16 (every shape but the narrow and phase-subset
+        // ones): its phase, channel base and row offsets are wave-uniform, and
+        // block cb + TCO/16 holds the next phase of the same channels, i.e. the
+        // next output element of a row, so the two values go out as one 4-byte
+        // LDS write when both phases sit in the same output row.
+        auto stage_pairs = [&](auto step_tag) __attribute__((always_inline)) {
+            constexpr int STEP = decltype(step_tag)::value;  // TCO / 16 (0: no pairing)
+            const int T0 = wm * RB * 16;
+    #pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const int blk = wn * CB + cb;
+                const int pb = (int)uniform((uint32_t)(blk * 16 / a.TCO));
+                if (pb >= a.PT) continue;
+                const int co_l = blk * 16 - pb * a.TCO + li;
+                const int by = pb / a.sx, bx = pb - by * a.sx;
+                // Blocks pair up as (cb, cb + STEP) for (cb / STEP) even; a pair is
+                // written together when the second block exists in the wave, holds
+                // a phase of the tile and that phase continues the same output row.
+                constexpr bool CAN = STEP > 0 && STEP < CB;
+                const bool first = CAN && ((cb / (CAN ? STEP : 1)) % 2 == 0) && cb + STEP < CB;
+                const bool second = CAN && ((cb / (CAN ? STEP : 1)) % 2 == 1);
+                const int cbp = first ? cb + STEP : cb;
+                const bool pair = first && pb + 1 < a.PT && bx + 1 < a.sx;
+                if (second && (pb - 1) - ((pb - 1) / a.sx) * a.sx + 1 < a.sx)
+                    continue;  // written together with the previous phase's block
+                const int co = co0 + co_l;
+                float bv = 0.f;
+                if (!a.atomic_out && biasg != nullptr && co < a.C_out) bv = TR::to_f32(biasg[co]);
+                // element offsets: lane part + wave-uniform part; the other
+                // terms of an offset are even, so its parity is that of
+                // bx + i*sx (wave-uniform)
+                const int lane_base = co_l * CSTR + lg * 4 * a.sx;
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            const int blk = wn * CB + cb;
-            const int pb = (int)uniform((uint32_t)(blk * 16 / a.TCO));
-            if (pb >= a.PT) continue;
-            const int co_l = blk * 16 - pb * a.TCO + li;
-            const int by = pb / a.sx, bx = pb - by * a.sx;
-            // Blocks pair up as (cb, cb + STEP) for (cb / STEP) even; a pair is
-            // written together when the second block exists in the wave, holds
-            // a phase of the tile and that phase continues the same output row.
-            constexpr bool CAN = STEP > 0 && STEP < CB;
-            const bool first = CAN && ((cb / (CAN ? STEP : 1)) % 2 == 0) && cb + STEP < CB;
-            const bool second = CAN && ((cb / (CAN ? STEP : 1)) % 2 == 1);
-            const int cbp = first ? cb + STEP : cb;
-            const bool pair = first && pb + 1 < a.PT && bx + 1 < a.sx;
-            if (second && (pb - 1) - ((pb - 1) / a.sx) * a.sx + 1 < a.sx)
-                continue;  // written together with the previous phase's block
-            const int co = co0 + co_l;
-            float bv = 0.f;
-            if (!a.atomic_out && biasg != nullptr && co < a.C_out) bv = TR::to_f32(biasg[co]);
-            const int lane_base = co_l * CSTR + lg * 4 * a.sx + bx;
+                for (int rb = 0; rb < RB; ++rb) {
+                    const int t = T0 + rb * 16;
+                    const int rowpart = (int)uniform(
+                        (uint32_t)(((t / TAX) * a.sy + by) * SS + (t % TAX) * a.sx + bx));
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                const int t = T0 + rb * 16;
-                const int rowpart = ((t / TAX) * a.sy + by) * SS + (t % TAX) * a.sx;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    S* dst = smem + lane_base + rowpart + i * a.sx;
-                    const S v0 = TR::from_f32(acc[rb][cb][i] + bv);
-                    if (pair) {
-                        const S v1 = TR::from_f32(acc[rb][cbp][i] + bv);
-                        if constexpr (sizeof(S) == 2) {
-                            // 4-byte aligned: output rows and phase pairs start even
-                            const uint32_t w = (uint32_t)__builtin_bit_cast(uint16_t, v0) |
-                                               ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
-                            if ((((uintptr_t)dst) & 3u) == 0u) {
-                                *reinterpret_cast<uint32_t*>(dst) = w;
+                    for (int i = 0; i < 4; ++i) {
+                        const int ui = (int)uniform((uint32_t)(rowpart + i * a.sx));
+                        const int off = lane_base + ui;
+                        const float f0 = actf(acc[rb][cb][i] + bv);
+                        if (pair) {
+                            const float f1 = actf(acc[rb][cbp][i] + bv);
+                            if constexpr (sizeof(S) == 2) {
+                                const uint32_t w = pack2<TR>(f0, f1);
+                                if ((ui & 1) == 0) {  // 4-byte aligned
+                                    *reinterpret_cast<uint32_t*>(smem + off) = w;
+                                } else {
+                                    smem[off] = (S)(w & 0xffffu);
+                                    smem[off + 1] = (S)(w >> 16);
+                                }
                             } else {
-                                dst[0] = v0;
-                                dst[1] = v1;
+                                smem[off] = f0;
+                                smem[off + 1] = f1;
                             }
                         } else {
-                            dst[0] = v0;
-                            dst[1] = v1;
+                            smem[off] = TR::from_f32(f0);
                         }
-                    } else {
-                        *dst = v0;
                     }
                 }
             }
+        };
+        if (!a.phase_subset && (a.TCO & 15) == 0 && a.TCO / 16 == 1) {
+            stage_pairs(std::integral_constant<int, 1>{});
+        } else if (!a.phase_subset && (a.TCO & 15) == 0 && a.TCO / 16 == 2) {
+            stage_pairs(std::integral_constant<int, 2>{});
+        } else if (!a.phase_subset && (a.TCO & 15) == 0) {
+            stage_pairs(std::integral_constant<int, 0>{});
+        } else {
+        #pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const int tc = bcol + cb * 16;
+                const int pb = tc / a.TCO, co_l = tc - (tc / a.TCO) * a.TCO;
+                if (pb >= a.PT) continue;
+                const int co = co0 + co_l;
+                float bv = 0.f;
+                if (!a.atomic_out && biasg != nullptr && co < a.C_out) bv = TR::to_f32(biasg[co]);
+                const int by = pb / a.sx, bx = pb - by * a.sx;
+        #pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+        #pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int tr = (wm * RB + rb) * 16 + lg * 4 + i;
+                        const int ayl = tr / TAX, axl = tr % TAX;
+                        int rr, ss;
+                        if (a.phase_subset) {
+                            rr = axl;
+                            ss = pb;
+                        } else {
+                            rr = ayl * a.sy + by;
+                            ss = axl * a.sx + bx;
+                        }
+                        smem[co_l * CSTR + rr * SS + ss] = TR::from_f32(actf(acc[rb][cb][i] + bv));
+                    }
+            }
         }
     };
-    if (!a.phase_subset && (a.TCO & 15) == 0 && a.TCO / 16 == 1) {
-        stage_pairs(std::integral_constant<int, 1>{});
-    } else if (!a.phase_subset && (a.TCO & 15) == 0 && a.TCO / 16 == 2) {
-        stage_pairs(std::integral_constant<int, 2>{});
-    } else if (!a.phase_subset && (a.TCO & 15) == 0) {
-        stage_pairs(std::integral_constant<int, 0>{});
-    } else {
-    #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-            const int tc = bcol + cb * 16;
-            const int pb = tc / a.TCO, co_l = tc - (tc / a.TCO) * a.TCO;
-            if (pb >= a.PT) continue;
-            const int co = co0 + co_l;
-            float bv = 0.f;
-            if (!a.atomic_out && biasg != nullptr && co < a.C_out) bv = TR::to_f32(biasg[co]);
-            const int by = pb / a.sx, bx = pb - by * a.sx;
-    #pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-    #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int tr = (wm * RB + rb) * 16 + lg * 4 + i;
-                    const int ayl = tr / TAX, axl = tr % TAX;
-                    int rr, ss;
-                    if (a.phase_subset) {
-                        rr = axl;
-                        ss = pb;
-                    } else {
-                        rr = ayl * a.sy + by;
-                        ss = axl * a.sx + bx;
-                    }
-                    smem[co_l * CSTR + rr * SS + ss] = TR::from_f32(acc[rb][cb][i] + bv);
-                }
-        }
-    }
+    if (a.act == CTCONV_ACT_ELU)
+        stage_all(std::true_type{});
+    else
+        stage_all(std::false_type{});
     __syncthreads();
 
     S* __restrict__ yg = static_cast<S*>(a.y);
@@ -1069,7 +1097,8 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
     if (per_cu < 1) per_cu = 1;
     const int64_t slots = 256 * per_cu;
     int best = 1;
-    if (p.dtype == CTCONV_F32 && tiles < 2 * slots && n_chunks >= 8) {
+    // (never with a fused activation: partial sums cannot be activated)
+    if (p.dtype == CTCONV_F32 && tiles < 2 * slots && n_chunks >= 8 && p.act == CTCONV_ACT_NONE) {
         double best_cost = 1e300;
         for (int sp = 1; sp <= 64 && sp <= n_chunks; ++sp) {
             const int64_t cps = (n_chunks + sp - 1) / sp;
@@ -1086,6 +1115,7 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
     a->atomic_out = best > 1 ? 1 : 0;
     a->xcd_remap = (tiles % 8 == 0) ? 1 : 0;
     a->pw_bytes = (uint32_t)pw_bytes;
+    a->act = p.act;
     *inst = in;
     *splits = best;
     return true;

@@ -21,9 +21,11 @@ STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_PARAM", 4: "ERR_DTYPE"
 
 EXPORTED = (
     "ctconv_abi_version", "ctconv_status_string", "ctconv_output_shape", "ctconv_packed_bytes",
-    "ctconv_prepack", "ctconv_forward", "ctconv_forward_route", "ctconv_query_route",
-    "ctconv_elu",
+    "ctconv_prepack", "ctconv_forward", "ctconv_forward_route", "ctconv_forward_act",
+    "ctconv_query_route", "ctconv_elu",
 )
+
+ACT_NONE, ACT_ELU = 0, 1
 
 
 class CtconvError(RuntimeError):
@@ -63,6 +65,8 @@ def load(path: str = LIB_PATH):
     lib.ctconv_forward.restype = c_int
     lib.ctconv_forward_route.argtypes = fwd + [c_int, c_vp]
     lib.ctconv_forward_route.restype = c_int
+    lib.ctconv_forward_act.argtypes = fwd + [c_int, c_int, c_vp]
+    lib.ctconv_forward_act.restype = c_int
     lib.ctconv_query_route.argtypes = [c_i64, c_i64, c_i64, c_int] + [_i64p] * 6 + [
         c_int, ctypes.POINTER(c_int)]
     lib.ctconv_query_route.restype = c_int
@@ -147,6 +151,19 @@ def ctconv_forward_route(x_ptr: int, packed_ptr: int, bias_ptr: Optional[int], y
     _check("ctconv_forward_route", st)
 
 
+def ctconv_forward_act(x_ptr: int, packed_ptr: int, bias_ptr: Optional[int], y_ptr: int, N: int,
+                       C_in: int, C_out: int, in_spatial, kernel, stride, padding,
+                       output_padding, dilation, dtype: int, act: int, route: int,
+                       stream: int) -> None:
+    ndim = len(in_spatial)
+    st = load().ctconv_forward_act(
+        x_ptr, packed_ptr, bias_ptr, y_ptr, N, C_in, C_out, ndim, _arr(in_spatial),
+        _arr(per_dim(kernel, ndim)), _arr(per_dim(stride, ndim)), _arr(per_dim(padding, ndim)),
+        _arr(per_dim(output_padding, ndim)), _arr(per_dim(dilation, ndim)), dtype, act, route,
+        stream)
+    _check("ctconv_forward_act", st)
+
+
 def ctconv_forward(x_ptr: int, packed_ptr: int, bias_ptr: Optional[int], y_ptr: int, N: int,
                    C_in: int, C_out: int, in_spatial, kernel, stride, padding, output_padding,
                    dilation, dtype: int, stream: int) -> None:
@@ -218,8 +235,8 @@ def prepack(w, stride, stream=None):
 
 
 def forward(x, packed, bias, C_out: int, kernel, stride, padding=0, output_padding=0,
-            dilation=1, route: int = ROUTE_AUTO, out=None, stream=None):
-    """y = ConvTranspose(x, w, bias) with w given by its packed form (device tensors)."""
+            dilation=1, route: int = ROUTE_AUTO, out=None, stream=None, act: int = ACT_NONE):
+    """y = act(ConvTranspose(x, w, bias)) with w given by its packed form (device tensors)."""
     torch = _torch()
     if not x.is_cuda:
         raise ValueError("x must be a device tensor")
@@ -230,9 +247,9 @@ def forward(x, packed, bias, C_out: int, kernel, stride, padding=0, output_paddi
     osp = ctconv_output_shape(sp, kernel, stride, padding, output_padding, dilation)
     y = out if out is not None else torch.empty((N, C_out) + osp, dtype=x.dtype, device=x.device)
     bptr = None if bias is None else bias.contiguous().data_ptr()
-    ctconv_forward_route(x.data_ptr(), packed.data_ptr(), bptr, y.data_ptr(), N, C_in, C_out, sp,
-                         kernel, stride, padding, output_padding, dilation, dtype_code(x), route,
-                         _stream(stream))
+    ctconv_forward_act(x.data_ptr(), packed.data_ptr(), bptr, y.data_ptr(), N, C_in, C_out, sp,
+                       kernel, stride, padding, output_padding, dilation, dtype_code(x), act,
+                       route, _stream(stream))
     return y
 
 
@@ -254,7 +271,7 @@ class Conv:
 
     def __init__(self, N: int, C_in: int, C_out: int, in_spatial, kernel, stride, padding=0,
                  output_padding=0, dilation=1, dtype: int = CTCONV_F32,
-                 route: int = ROUTE_AUTO):
+                 route: int = ROUTE_AUTO, act: int = ACT_NONE):
         nd = len(in_spatial)
         self.ndim = nd
         self.N, self.C_in, self.C_out = int(N), int(C_in), int(C_out)
@@ -266,17 +283,18 @@ class Conv:
         self.dilation = per_dim(dilation, nd)
         self.dtype = dtype
         self.route = route
+        self.act = act
         self.out_spatial = ctconv_output_shape(self.in_spatial, self.kernel, self.stride,
                                                self.padding, self.output_padding, self.dilation)
         self._args = [_arr(self.in_spatial), _arr(self.kernel), _arr(self.stride),
                       _arr(self.padding), _arr(self.output_padding), _arr(self.dilation)]
-        self._fn = load().ctconv_forward_route
+        self._fn = load().ctconv_forward_act
 
     def out_shape(self):
         return (self.N, self.C_out) + self.out_spatial
 
     def __call__(self, x_ptr: int, packed_ptr: int, bias_ptr, y_ptr: int, stream: int) -> None:
         st = self._fn(x_ptr, packed_ptr, bias_ptr, y_ptr, self.N, self.C_in, self.C_out,
-                      self.ndim, *self._args, self.dtype, self.route, stream)
+                      self.ndim, *self._args, self.dtype, self.act, self.route, stream)
         if st != 0:
-            raise CtconvError("ctconv_forward_route", st)
+            raise CtconvError("ctconv_forward_act", st)
