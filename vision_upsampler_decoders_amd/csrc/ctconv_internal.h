@@ -94,6 +94,27 @@ __device__ inline float elu_act(float v) {
 
 constexpr int64_t kCinAlign = 32;
 
+// Division by a launch-constant divisor d >= 1 as a multiply and a shift:
+// q = floor(n * m / 2^s) with s = 31 + ceil(log2 d) and m = ceil(2^s / d)
+// (below 2^32).  m exceeds 2^s / d by e < 1, so n * m / 2^s exceeds n / d by
+// n * e / 2^s < 2^31 / 2^s <= 1 / d, which never reaches the next integer
+// for 0 <= n < 2^31.
+struct FastDiv {
+    uint32_t m, s;
+};
+
+inline FastDiv make_fastdiv(uint32_t d) {
+    uint32_t l = 0;
+    while (l < 32 && (1ull << l) < d) ++l;
+    const uint32_t s = 31 + l;
+    const uint64_t pw = 1ull << s;
+    return FastDiv{(uint32_t)((pw + d - 1) / d), s};
+}
+
+__device__ inline uint32_t fdiv(uint32_t n, FastDiv f) {
+    return (uint32_t)(((uint64_t)n * f.m) >> f.s);
+}
+
 // Arguments of the polyphase MFMA kernel (filled by the host planner).
 struct PolyArgs {
     const void* x;
@@ -116,6 +137,10 @@ struct PolyArgs {
     int n_ph_tiles, n_col_tiles;
     int tiles_y, tiles_x;
     int64_t n_row_tiles;
+    uint32_t n_tiles;      // row tiles x column tiles (below 2^31): the grid
+    // divisions by launch constants (tile decomposition, window rows, column
+    // tile channels, strides, staged output rows)
+    FastDiv fd_cols, fd_ph, fd_tx, fd_ty, fd_wy, fd_tco, fd_sx, fd_sy, fd_R;
     int n_chunks;          // C_in_pad / KC
     int chunks_per_split;  // split over C_in: each blockIdx.y takes this many chunks
     int atomic_out;        // 1: accumulate with fp32 atomics into a pre-filled y

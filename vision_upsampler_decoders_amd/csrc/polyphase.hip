@@ -212,19 +212,22 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     const S* __restrict__ pwg = static_cast<const S*>(a.pw);
 
     // ---- tile coordinates -------------------------------------------------
-    int64_t bid = blockIdx.x;
-    if (a.xcd_remap) {
-        const int64_t per = gridDim.x / 8;
-        bid = (bid % 8) * per + bid / 8;
-    }
-    const int col_tile = (int)(bid % a.n_col_tiles);
-    const int64_t row_tile = bid / a.n_col_tiles;
-    const int tx_t = (int)(row_tile % a.tiles_x);
-    const int64_t rt2 = row_tile / a.tiles_x;
-    const int ty_t = (int)(rt2 % a.tiles_y);
-    const int64_t n = rt2 / a.tiles_y;
-    const int co0 = (col_tile / a.n_ph_tiles) * a.TCO;
-    const int b0 = (col_tile % a.n_ph_tiles) * a.PT;
+    // linear tile = ((n * tiles_y + ty) * tiles_x + tx) * n_col_tiles + col;
+    // with the XCD remap the gridDim.x / 8 workgroups of one XCD (dispatched
+    // round robin) take a contiguous run of tiles, so that the column tiles
+    // of one row tile, which read the same input rows, meet in one L2
+    uint32_t bid = blockIdx.x;
+    if (a.xcd_remap) bid = (bid % 8u) * (gridDim.x / 8u) + bid / 8u;
+    const uint32_t row_tile = fdiv(bid, a.fd_cols);
+    const int col_tile = (int)(bid - row_tile * (uint32_t)a.n_col_tiles);
+    const uint32_t rt2 = fdiv(row_tile, a.fd_tx);
+    const int tx_t = (int)(row_tile - rt2 * (uint32_t)a.tiles_x);
+    const uint32_t nq = fdiv(rt2, a.fd_ty);
+    const int ty_t = (int)(rt2 - nq * (uint32_t)a.tiles_y);
+    const int64_t n = nq;
+    const int cq = (int)fdiv((uint32_t)col_tile, a.fd_ph);
+    const int co0 = cq * a.TCO;
+    const int b0 = (col_tile - cq * a.n_ph_tiles) * a.PT;
     const int ay0 = ty_t * C::TAY, ax0 = tx_t * TAX;
     const int wy0 = ay0 + a.dminy - (MY - 1);
     const int wx0 = ax0 + a.dminx - (MX - 1) - a.xofs;
@@ -275,8 +278,8 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
         if (qw < xper && q < xitems) {
             const int gx = q % ngx;
             const int r2 = q / ngx;
-            const int wy = r2 % a.WY;
-            const int g = r2 / a.WY;
+            const int g = (int)fdiv((uint32_t)r2, a.fd_wy);
+            const int wy = r2 - g * a.WY;
             const int iy = wy0 + wy;
             const bool rowok = iy >= 0 && iy < a.H;
             const int p0 = wx0 + gx * NP;
@@ -338,10 +341,13 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
         if (qw < bper && q < C::BMAX) {
             const int row = q / NG, piece = q % NG;
             const int r = row / BN, tc = row % BN;
-            const int pb = tc / a.TCO, co = co0 + tc % a.TCO, b = b0 + pb;
+            const int pb = (int)fdiv((uint32_t)tc, a.fd_tco);
+            const int co = co0 + tc - pb * a.TCO, b = b0 + pb;
             if (pb < a.PT && b < a.P && co < a.C_out) {
-                const int by = b / a.sx, bx = b % a.sx;
-                const int j = ((by + a.py) % a.sy) * a.sx + (bx + a.px) % a.sx;
+                const int by = (int)fdiv((uint32_t)b, a.fd_sx), bx = b - by * a.sx;
+                const int jy = by + a.py - (int)fdiv((uint32_t)(by + a.py), a.fd_sy) * a.sy;
+                const int jx = bx + a.px - (int)fdiv((uint32_t)(bx + a.px), a.fd_sx) * a.sx;
+                const int j = jy * a.sx + jx;
                 // packed layout [j][ci / 32][co][r][ci % 32]: row (co, r) of
                 // phase j in channel block 0 (the chunk adds its block)
                 boff[it] = (uint32_t)((((int64_t)j * (a.C_in_pad / kCinAlign) * a.C_out + co) * T +
@@ -356,12 +362,12 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
         const int tc0 = (wn * CB + cb) * 16;
-        const int pb = tc0 / a.TCO, b = b0 + pb;
+        const int pb = (int)fdiv((uint32_t)tc0, a.fd_tco), b = b0 + pb;
         int dy = 0, dx = 0;
         if (pb < a.PT && b < a.P) {
-            const int by = b / a.sx, bx = b % a.sx;
-            dy = (by + a.py) / a.sy - a.dminy;
-            dx = (bx + a.px) / a.sx - a.dminx;
+            const int by = (int)fdiv((uint32_t)b, a.fd_sx), bx = b - by * a.sx;
+            dy = (int)fdiv((uint32_t)(by + a.py), a.fd_sy) - a.dminy;
+            dx = (int)fdiv((uint32_t)(bx + a.px), a.fd_sx) - a.dminx;
         }
         ddy[cb] = __builtin_amdgcn_readfirstlane(dy);
         ddx[cb] = __builtin_amdgcn_readfirstlane(dx);
@@ -745,10 +751,10 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
                 const int blk = wn * CB + cb;
-                const int pb = (int)uniform((uint32_t)(blk * 16 / a.TCO));
+                const int pb = (int)uniform(fdiv((uint32_t)(blk * 16), a.fd_tco));
                 if (pb >= a.PT) continue;
                 const int co_l = blk * 16 - pb * a.TCO + li;
-                const int by = pb / a.sx, bx = pb - by * a.sx;
+                const int by = (int)fdiv((uint32_t)pb, a.fd_sx), bx = pb - by * a.sx;
                 // Blocks pair up as (cb, cb + STEP) for (cb / STEP) even; a pair is
                 // written together when the second block exists in the wave, holds
                 // a phase of the tile and that phase continues the same output row.
@@ -757,7 +763,7 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                 const bool second = CAN && ((cb / (CAN ? STEP : 1)) % 2 == 1);
                 const int cbp = first ? cb + STEP : cb;
                 const bool pair = first && pb + 1 < a.PT && bx + 1 < a.sx;
-                if (second && (pb - 1) - ((pb - 1) / a.sx) * a.sx + 1 < a.sx)
+                if (second && (pb - 1) - (int)fdiv((uint32_t)(pb - 1), a.fd_sx) * a.sx + 1 < a.sx)
                     continue;  // written together with the previous phase's block
                 const int co = co0 + co_l;
                 float bv = 0.f;
@@ -807,12 +813,12 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
         #pragma unroll
             for (int cb = 0; cb < CB; ++cb) {
                 const int tc = bcol + cb * 16;
-                const int pb = tc / a.TCO, co_l = tc - (tc / a.TCO) * a.TCO;
+                const int pb = (int)fdiv((uint32_t)tc, a.fd_tco), co_l = tc - pb * a.TCO;
                 if (pb >= a.PT) continue;
                 const int co = co0 + co_l;
                 float bv = 0.f;
                 if (!a.atomic_out && biasg != nullptr && co < a.C_out) bv = TR::to_f32(biasg[co]);
-                const int by = pb / a.sx, bx = pb - by * a.sx;
+                const int by = (int)fdiv((uint32_t)pb, a.fd_sx), bx = pb - by * a.sx;
         #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
         #pragma unroll
@@ -842,7 +848,7 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     const int nrows = a.TCO * R;
     const bool vec_ok = (SS % VEC) == 0 && !a.atomic_out;
     for (int row = wave; row < nrows; row += C::NW) {
-        const int co_l = row / R, rr = row - (row / R) * R;
+        const int co_l = (int)fdiv((uint32_t)row, a.fd_R), rr = row - co_l * R;
         const int co = co0 + co_l;
         if (co >= a.C_out) continue;
         int64_t oy, ox0;
@@ -1114,6 +1120,16 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
     a->chunks_per_split = (int)((n_chunks + best - 1) / best);
     a->atomic_out = best > 1 ? 1 : 0;
     a->xcd_remap = (tiles % 8 == 0) ? 1 : 0;
+    a->n_tiles = (uint32_t)tiles;
+    a->fd_cols = make_fastdiv((uint32_t)n_col_tiles);
+    a->fd_ph = make_fastdiv((uint32_t)n_ph_tiles);
+    a->fd_tx = make_fastdiv((uint32_t)tiles_x);
+    a->fd_ty = make_fastdiv((uint32_t)tiles_y);
+    a->fd_wy = make_fastdiv((uint32_t)a->WY);
+    a->fd_tco = make_fastdiv((uint32_t)TCO);
+    a->fd_sx = make_fastdiv((uint32_t)p.sW);
+    a->fd_sy = make_fastdiv((uint32_t)p.sH);
+    a->fd_R = make_fastdiv((uint32_t)(subset ? in.TAX : in.TAY * p.sH));
     a->pw_bytes = (uint32_t)pw_bytes;
     a->act = p.act;
     *inst = in;
@@ -1144,7 +1160,7 @@ hipError_t launch_polyphase(const Problem& p, const void* x, const void* pw, con
         const hipError_t e = launch_fill(p, bias, y, s);
         if (e != hipSuccess) return e;
     }
-    const int64_t tiles = a.n_row_tiles * a.n_col_tiles;
+    const int64_t tiles = a.n_tiles;
     hipLaunchKernelGGL(in.fn, dim3((unsigned)tiles, (unsigned)splits), dim3(in.threads), 0, s, a);
     return hipGetLastError();
 }
