@@ -139,8 +139,9 @@ struct PolyArgs {
     int64_t n_row_tiles;
     uint32_t n_tiles;      // row tiles x column tiles (below 2^31): the grid
     // divisions by launch constants (tile decomposition, window rows, column
-    // tile channels, strides, staged output rows)
+    // tile channels, strides, staged output rows and their 16-byte chunks)
     FastDiv fd_cols, fd_ph, fd_tx, fd_ty, fd_wy, fd_tco, fd_sx, fd_sy, fd_R;
+    FastDiv fd_cpr;        // 16-byte chunks per staged output row
     int n_chunks;          // C_in_pad / KC
     int chunks_per_split;  // split over C_in: each blockIdx.y takes this many chunks
     int atomic_out;        // 1: accumulate with fp32 atomics into a pre-filled y

@@ -847,6 +847,50 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     S* __restrict__ yg = static_cast<S*>(a.y);
     const int nrows = a.TCO * R;
     const bool vec_ok = (SS % VEC) == 0 && !a.atomic_out;
+    if (vec_ok && !a.phase_subset) {
+        // Flattened over the tile: chunk e (VEC elements) is row e / cpr,
+        // column chunk e % cpr of the staged output, so consecutive lanes
+        // take consecutive chunks (a short row does not idle a wave's other
+        // lanes) and each thread reads U chunks from LDS before it stores
+        // them (one LDS latency per U stores).
+        const int cpr = SS / VEC;
+        const int total = nrows * cpr;
+        const int64_t ox0 = (int64_t)ax0 * a.sx;
+        const int lim = (int)min((int64_t)SS, a.Wo - ox0);  // valid elements of a row
+        constexpr int U = 4;
+        for (int e0 = tid; e0 < total; e0 += U * C::NT) {
+            u32x4 v[U];
+            int64_t gb[U];
+            int s0v[U], sof[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int e = e0 + u * C::NT;
+                const int ec = e < total ? e : 0;
+                const int row = (int)fdiv((uint32_t)ec, a.fd_cpr);
+                const int s0 = (ec - row * cpr) * VEC;
+                const int co_l = (int)fdiv((uint32_t)row, a.fd_R), rr = row - co_l * R;
+                const int co = co0 + co_l;
+                const int64_t oy = (int64_t)ay0 * a.sy + rr;
+                ok[u] = e < total && co < a.C_out && oy < a.Ho && s0 < lim;
+                sof[u] = co_l * CSTR + rr * SS;
+                s0v[u] = s0;
+                gb[u] = ((n * a.C_out + co) * a.Ho + oy) * a.Wo + ox0;
+                v[u] = *reinterpret_cast<const u32x4*>(smem + sof[u] + s0);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (!ok[u]) continue;
+                const int s0 = s0v[u];
+                if (s0 + VEC <= lim) {
+                    store16_unaligned(yg + gb[u] + s0, v[u]);
+                } else {
+                    for (int q = s0; q < lim; ++q) yg[gb[u] + q] = smem[sof[u] + q];
+                }
+            }
+        }
+        return;
+    }
     for (int row = wave; row < nrows; row += C::NW) {
         const int co_l = (int)fdiv((uint32_t)row, a.fd_R), rr = row - co_l * R;
         const int co = co0 + co_l;
@@ -1130,6 +1174,12 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
     a->fd_sx = make_fastdiv((uint32_t)p.sW);
     a->fd_sy = make_fastdiv((uint32_t)p.sH);
     a->fd_R = make_fastdiv((uint32_t)(subset ? in.TAX : in.TAY * p.sH));
+    {
+        // staged-row chunks of 16 bytes (flattened output stores)
+        const int64_t vec = p.dtype == CTCONV_F32 ? 4 : 8;
+        const int64_t cpr = (in.TAX * p.sW) / vec;
+        a->fd_cpr = make_fastdiv((uint32_t)(cpr > 0 ? cpr : 1));
+    }
     a->pw_bytes = (uint32_t)pw_bytes;
     a->act = p.act;
     *inst = in;
