@@ -61,6 +61,7 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_u __attribute__((ext_vector_type(4), aligned(1)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32_a2 __attribute__((aligned(2)));
 
 template <class TR>
 struct Mma;
@@ -500,6 +501,30 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     }
     const int bcol = (wn * CB) * 16 + li;
 
+    // Bias of each column block's output channel, loaded now so that the
+    // epilogue never waits for it.  One unconditional load per block: a
+    // column past the phases or past C_out, a split-over-C_in launch (whose
+    // bias is in the pre-filled output) and a missing bias all read past the
+    // resource's range, which returns zero.
+    float bvs[CB];
+    {
+        const bool has_bias = a.bias != nullptr && !a.atomic_out;
+        const __amdgpu_buffer_rsrc_t bres = __builtin_amdgcn_make_buffer_rsrc(
+            uniform_ptr(has_bias ? a.bias : a.pw), (short)0,
+            (int)uniform(has_bias ? (uint32_t)(a.C_out * C::ES) : 0u), kBufferWord3);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+            const int tc = bcol + cb * 16;
+            const int pb = (int)fdiv((uint32_t)tc, a.fd_tco);
+            const int co = co0 + tc - pb * a.TCO;
+            const uint32_t off = (pb < a.PT && co < a.C_out) ? (uint32_t)co * C::ES : 0x7FFFFFF0u;
+            if constexpr (C::ES == 2)
+                bvs[cb] = TR::to_f32(__builtin_amdgcn_raw_buffer_load_b16(bres, off, 0, 0));
+            else
+                bvs[cb] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bres, off, 0, 0));
+        }
+    }
+
     // Shift bookkeeping: column block cb belongs to class (dd_y, dd_x) with
     // dd in {0, 1} per dimension; for tap (ry, rx) its A rows sit at window
     // offset (dd_y + MY-1-ry, dd_x + MX-1-rx).  Classes and their presence
@@ -725,7 +750,6 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     __syncthreads();
 
     // ---- epilogue: bias, round, stage in output order, store ---------------
-    const S* __restrict__ biasg = static_cast<const S*>(a.bias);
     const int R = a.phase_subset ? TAX : C::TAY * a.sy;
     const int SS = a.phase_subset ? a.PT : TAX * a.sx;
     // output-channel stride padded by 16 bytes: lanes of one MFMA column block
@@ -766,11 +790,8 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                 if (second && (pb - 1) - (int)fdiv((uint32_t)(pb - 1), a.fd_sx) * a.sx + 1 < a.sx)
                     continue;  // written together with the previous phase's block
                 const int co = co0 + co_l;
-                float bv = 0.f;
-                if (!a.atomic_out && biasg != nullptr && co < a.C_out) bv = TR::to_f32(biasg[co]);
-                // element offsets: lane part + wave-uniform part; the other
-                // terms of an offset are even, so its parity is that of
-                // bx + i*sx (wave-uniform)
+                const float bv = bvs[cb];
+                // element offsets: lane part + wave-uniform part
                 const int lane_base = co_l * CSTR + lg * 4 * a.sx;
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
@@ -785,13 +806,9 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                         if (pair) {
                             const float f1 = actf(acc[rb][cbp][i] + bv);
                             if constexpr (sizeof(S) == 2) {
-                                const uint32_t w = pack2<TR>(f0, f1);
-                                if ((ui & 1) == 0) {  // 4-byte aligned
-                                    *reinterpret_cast<uint32_t*>(smem + off) = w;
-                                } else {
-                                    smem[off] = (S)(w & 0xffffu);
-                                    smem[off + 1] = (S)(w >> 16);
-                                }
+                                // one 4-byte LDS store at 2-byte alignment
+                                // (gfx950 LDS takes unaligned dword accesses)
+                                *reinterpret_cast<u32_a2*>(smem + off) = pack2<TR>(f0, f1);
                             } else {
                                 smem[off] = f0;
                                 smem[off + 1] = f1;
@@ -816,8 +833,7 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                 const int pb = (int)fdiv((uint32_t)tc, a.fd_tco), co_l = tc - pb * a.TCO;
                 if (pb >= a.PT) continue;
                 const int co = co0 + co_l;
-                float bv = 0.f;
-                if (!a.atomic_out && biasg != nullptr && co < a.C_out) bv = TR::to_f32(biasg[co]);
+                const float bv = bvs[cb];
                 const int by = (int)fdiv((uint32_t)pb, a.fd_sx), bx = pb - by * a.sx;
         #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
