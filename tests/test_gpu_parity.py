@@ -139,6 +139,11 @@ FULL_CASES = [
     ("k5_s4_op3_f16", "f16", 2, 40, 20, (130,), (5,), (4,), (1,), (3,), (1,), False),
     ("k3_s2_op1_2d_f32", "f32", 2, 24, 12, (13, 17), (3, 3), (2, 2), (0, 1), (1, 1), (1, 1), True),
     ("k3x4_s2x3_2d_bf16", "bf16", 1, 40, 24, (12, 15), (3, 4), (2, 3), (1, 0), (0, 2), (1, 1), True),
+    # three and four taps in 16-bit storage (eight-wave tiles), five phases
+    # with three and four taps (256 x 160 tiles), odd and even lengths
+    ("s5_m3_op2_bf16", "bf16", 2, 72, 40, (257,), (13,), (5,), (4,), (2,), (1,), True),
+    ("s5_m4_f16", "f16", 1, 40, 30, (300,), (20,), (5,), (7,), (0,), (1,), False),
+    ("s4_m4_bf16", "bf16", 2, 64, 48, (400,), (16,), (4,), (6,), (0,), (1,), True),
 ]
 
 

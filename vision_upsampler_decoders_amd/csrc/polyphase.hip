@@ -965,10 +965,12 @@ Inst make_inst() {
                 C::KC, C::NT, (int)(C::SMEM * C::ES)};
 }
 
-// Tile shapes.  16-bit storage: 256 output rows x 128 columns, eight waves of
-// 64 x 64 each, two per SIMD, one workgroup per CU; five-phase shapes: 128 x
-// 160 with four waves of 64 x 80, two workgroups per CU.  fp32: 128 x 128
-// with eight waves of 64 x 32.
+// Tile shapes.  16-bit storage, 1-D with one or two taps: 128 output rows x
+// 128 columns (x 160 for five-phase shapes), four waves of 64 x 64 (64 x 80),
+// two workgroups per CU so that one's setup, first loads and epilogue overlap
+// the other's chunk loop; three or four taps: 256 rows, eight waves, one
+// workgroup per CU; 2-D: 4 x 64 rows x 128 columns, eight waves of 64 x 64.
+// fp32: 128 x 128 with eight waves of 64 x 32.
 #ifndef CTCONV_TILE_VARIANT
 #define CTCONV_TILE_VARIANT 2
 #endif
@@ -983,11 +985,11 @@ Inst inst_1d() {
             return make_inst<TR, MY, MX, 256, 4, 4, 4, 2, 2, XO>();
         else if constexpr (CTCONV_TILE_VARIANT == 5 && CB == 4 && MY * MX <= 2)
             return make_inst<TR, MY, MX, 256, 4, 8, 4, 2, 1, XO>();
-        else if constexpr (CB == 5)
-            // five-phase column tiles do not take the fused step; two 4-wave
-            // workgroups per CU overlap one's epilogue with the other's loop
-            return make_inst<TR, MY, MX, 128, 4, 5, 2, 2, 1, XO>();
+        else if constexpr (MY * MX <= 2)
+            return make_inst<TR, MY, MX, 128, 4, CB, 2, 2, 1, XO>();
         else
+            // three or four taps: a 4-wave tile would stage twice the weight
+            // rows per wave and drop to one wave per SIMD
             return make_inst<TR, MY, MX, 256, 4, CB, 4, 2, 1, XO>();
     } else {
         return make_inst<TR, MY, MX, 128, 4, 2, 2, 4, 1, XO>();
