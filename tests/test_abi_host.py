@@ -5,8 +5,9 @@
   invalid parameters;
 * ctconv_packed_bytes follows the documented packed layout size;
 * argument validation returns the documented status before any launch;
-* routing: shapes with dilation 1 take the polyphase kernel (within its
-  compiled tap counts and row widths), the rest the gather kernel.
+* routing: shapes whose dilation divides the stride take the polyphase
+  kernel (within its compiled tap counts and row widths), the rest the
+  gather kernel.
 """
 
 import ctypes
@@ -134,7 +135,8 @@ def test_forward_validation_before_launch(lib):
     assert _fwd(lib, y=0x3008) == 5
     assert _fwd(lib, b=0x4004) == 5
     # polyphase forced on a shape outside the polyphase form
-    assert _fwd(lib, d=2, k=4, route=1) == 3
+    assert _fwd(lib, d=2, k=4, s=3, route=1) == 3    # dilation not dividing the stride
+    assert _fwd(lib, d=2, k=9, s=2, route=1) == 3    # reduced problem with 9 taps
     assert _fwd(lib, k=20, s=4, p=2, route=1) == 3   # 5 taps per phase
     assert _fwd(lib, sp=(3,), dt=1, route=1) == 3     # rows shorter than 8 bytes
     # fused activation: an unknown activation is rejected
@@ -154,7 +156,7 @@ def test_forward_with_N_zero_enqueues_nothing(lib):
 
 @pytest.mark.parametrize("name,route", [
     ("upsampler1d_small", 1), ("vocoder_stack", 1), ("istft", 1), ("upsampler2d", 1),
-    ("gather2d", 1), ("gather2d_dil2", 2),
+    ("gather2d", 1), ("gather2d_dil2", 1),
 ])
 def test_routes_of_workloads(lib, name, route):
     from synth import inputs as I
@@ -174,10 +176,25 @@ def test_routes_of_workloads(lib, name, route):
     (8, 4, 2, 0, 1, 1), (6, 3, 0, 0, 1, 1), (4, 1, 1, 0, 1, 1), (3, 2, 1, 0, 1, 1),
     (8, 4, 2, 1, 1, 1), (8, 4, 2, 0, 2, 2), (16, 4, 2, 0, 1, 1), (20, 4, 2, 0, 1, 2),
     (7, 3, 2, 2, 1, 1), (13, 4, 1, 0, 1, 1), (17, 4, 1, 0, 1, 2),
+    (3, 2, 1, 1, 2, 2), (4, 4, 1, 0, 2, 2), (5, 2, 1, 0, 3, 2),
 ])
 def test_route_rule(lib, k, s, p, op, d, route):
-    # polyphase iff d == 1 and m = ceil(k / s) within the compiled taps
+    # 1-D: polyphase iff d == 1 and m = ceil(k / s) within the compiled taps
     assert C.ctconv_query_route(2, 16, 16, (50,), k, s, p, op, d, 1) == route
+
+
+@pytest.mark.parametrize("k,s,p,op,d,route", [
+    ((3, 3), (2, 2), (1, 1), (1, 1), (2, 2), 1),   # reduced: stride 1, 3 x 3 taps
+    ((3, 3), (4, 4), (1, 1), (0, 0), (2, 2), 2),   # reduced: stride 2, 2 x 2 taps
+    ((3, 3), (3, 3), (1, 1), (0, 0), (2, 2), 2),   # d does not divide s
+    ((3, 3), (1, 1), (1, 1), (0, 0), (1, 1), 1),   # 3 x 3 taps without dilation
+    ((5, 5), (2, 2), (2, 2), (1, 1), (1, 1), 1),   # 3 x 3 taps per phase
+])
+def test_route_rule_2d_dilation(lib, k, s, p, op, d, route):
+    # 2-D: dilation d dividing s reduces to stride s / d with
+    # m = ceil(k / (s / d)) taps per dimension; the instances that run a
+    # reduced problem are the 3 x 3-tap ones
+    assert C.ctconv_query_route(2, 16, 16, (20, 22), k, s, p, op, d, 0) == route
 
 
 @pytest.mark.parametrize("sp,dt,route", [

@@ -144,6 +144,14 @@ FULL_CASES = [
     ("s5_m3_op2_bf16", "bf16", 2, 72, 40, (257,), (13,), (5,), (4,), (2,), (1,), True),
     ("s5_m4_f16", "f16", 1, 40, 30, (300,), (20,), (5,), (7,), (0,), (1,), False),
     ("s4_m4_bf16", "bf16", 2, 64, 48, (400,), (16,), (4,), (6,), (0,), (1,), True),
+    # dilation dividing the stride: 2-D 3 x 3 reduced taps on the polyphase
+    # route (the reduced problem of stride s / d; every other output is the
+    # bias) in fp32 and in 16-bit with odd rows; 1-D on the gather route
+    ("dil2_s2_2d_f32", "f32", 1, 24, 20, (13, 17), (3, 3), (2, 2), (1, 1), (1, 1), (2, 2), True),
+    ("dil2_s2_2d_bf16_odd", "bf16", 1, 40, 24, (9, 11), (3, 3), (2, 2), (0, 1), (0, 1), (2, 2),
+     True),
+    ("dil2_s4_bf16", "bf16", 2, 40, 24, (101,), (8,), (4,), (3,), (1,), (2,), True),
+    ("dil3_s3_k4_f16", "f16", 2, 33, 17, (90,), (4,), (3,), (2,), (2,), (3,), False),
 ]
 
 
@@ -267,6 +275,7 @@ ACT_CASES = [
     ("act_voc_l1", "bf16", 2, 512, 64, (120,), (16,), (8,), (4,), (0,), (1,), False),
     ("act_f32_2d", "f32", 2, 24, 20, (13, 11), (4, 4), (2, 2), (1, 1), (0, 0), (1, 1), True),
     ("act_f16_gather_dil", "f16", 1, 40, 12, (37,), (5,), (3,), (2,), (1,), (2,), True),
+    ("act_dil2_2d_f32", "f32", 1, 24, 20, (13, 11), (3, 3), (2, 2), (1, 1), (1, 1), (2, 2), True),
 ]
 
 

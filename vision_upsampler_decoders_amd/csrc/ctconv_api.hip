@@ -119,9 +119,10 @@ ctconv_status build_problem(int64_t N, int64_t C_in, int64_t C_out, int ndim,
 }
 
 bool polyphase_eligible(const Problem& p) {
-    // No dilation.  Any k: with m = ceil(k / s) taps per phase the packed
-    // weight's taps past k are zero; output_padding only lengthens the output.
-    return p.dH == 1 && p.dW == 1;
+    // Any k: with m = ceil(k / s) taps per phase the packed weight's taps past
+    // k are zero; output_padding only lengthens the output.  Dilation when it
+    // divides the stride (the kernel runs the reduced problem of stride s / d).
+    return (p.dH == 1 || p.sH % p.dH == 0) && (p.dW == 1 || p.sW % p.dW == 0);
 }
 
 ctconv_route choose_route(const Problem& p) {

@@ -142,12 +142,24 @@ struct PolyArgs {
     // tile channels, strides, staged output rows and their 16-byte chunks)
     FastDiv fd_cols, fd_ph, fd_tx, fd_ty, fd_wy, fd_tco, fd_sx, fd_sy, fd_R;
     FastDiv fd_cpr;        // 16-byte chunks per staged output row
+    FastDiv fd_psy, fd_psx;  // strides of the packed weight
     int n_chunks;          // C_in_pad / KC
     int chunks_per_split;  // split over C_in: each blockIdx.y takes this many chunks
     int atomic_out;        // 1: accumulate with fp32 atomics into a pre-filled y
     int xcd_remap;         // 1: gridDim.x is a multiple of 8, remap for L2 locality
     uint32_t pw_bytes;     // size of the packed weight (below 2^32)
     int act;               // ctconv_activation of the epilogue
+    // Dilation d dividing s (per dimension): the kernel runs the reduced
+    // problem (stride s/d, dilation 1) whose output u' sits at o0 + g*u' of
+    // the real output (g = d); the other outputs are bias only (pre-filled).
+    // Identity (g = 1, o0 = 0, real sizes = Ho, Wo) without dilation.
+    int gy, gx, o0y, o0x;
+    int64_t HoR, WoR;      // real output sizes (addressing of y)
+    // Packed-weight geometry (the real stride and taps the weight was packed
+    // with): effective tap (s_e*r + j) per dimension is real tap t, stored as
+    // phase t mod ps, tap t / ps; taps t >= k read as zero.
+    int psy, psx, pmx, pT, kH, kW;
+    uint32_t pw_cblock;    // bytes of one 32-channel block of a phase (C_out * pT * 32)
 };
 
 // Launchers (each returns hipGetLastError() of its launch).

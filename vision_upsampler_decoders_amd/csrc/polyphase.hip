@@ -199,7 +199,8 @@ struct Cfg {
 // 2-byte-misaligned 8-byte load costs the texture path per lane).
 // At least two waves per SIMD (256 registers per wave): an 8-wave workgroup
 // per CU, or two 4-wave ones; only 128 x 128 wave tiles need the whole file.
-template <class TR, int MY, int MX, int TAX, int RB, int CB, int WM, int WN, int KS, bool XODD>
+template <class TR, int MY, int MX, int TAX, int RB, int CB, int WM, int WN, int KS, bool XODD,
+          bool DIL>
 __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_kernel(
     const PolyArgs a) {
     using C = Cfg<TR, MY, MX, TAX, RB, CB, WM, WN, KS>;
@@ -348,11 +349,31 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                 const int by = (int)fdiv((uint32_t)b, a.fd_sx), bx = b - by * a.sx;
                 const int jy = by + a.py - (int)fdiv((uint32_t)(by + a.py), a.fd_sy) * a.sy;
                 const int jx = bx + a.px - (int)fdiv((uint32_t)(bx + a.px), a.fd_sx) * a.sx;
-                const int j = jy * a.sx + jx;
-                // packed layout [j][ci / 32][co][r][ci % 32]: row (co, r) of
-                // phase j in channel block 0 (the chunk adds its block)
-                boff[it] = (uint32_t)((((int64_t)j * (a.C_in_pad / kCinAlign) * a.C_out + co) * T +
-                                       r) * kCinAlign + piece * VEC) * C::ES;
+                if (!DIL || (a.gy == 1 && a.gx == 1)) {
+                    // packed layout [j][ci / 32][co][r][ci % 32]: row (co, r)
+                    // of phase j in channel block 0 (the chunk adds its block)
+                    boff[it] = (uint32_t)(((((int64_t)(jy * a.sx + jx) * (a.C_in_pad / kCinAlign) *
+                                                 a.C_out + co) * T + r) * kCinAlign +
+                                           piece * VEC) * C::ES);
+                } else if constexpr (DIL) {
+                    // dilation-reduced problem: its tap (ry, rx) of weight phase
+                    // (jy, jx) is real tap (ty, tx), packed as phase (ty mod psy,
+                    // tx mod psx), tap (ty / psy, tx / psx); taps past k read as
+                    // zero (an offset past the packed weight, which is below
+                    // 2^31 bytes: the range check of the load returns zeros)
+                    const int ty = a.sy * (r / MX) + jy, tx = a.sx * (r % MX) + jx;
+                    if (ty < a.kH && tx < a.kW) {
+                        const int qy = (int)fdiv((uint32_t)ty, a.fd_psy);
+                        const int qx = (int)fdiv((uint32_t)tx, a.fd_psx);
+                        const int jp = (ty - qy * a.psy) * a.psx + (tx - qx * a.psx);
+                        const int rp = qy * a.pmx + qx;
+                        boff[it] = (uint32_t)((((int64_t)jp * (a.C_in_pad / kCinAlign) * a.C_out +
+                                                co) * a.pT + rp) * kCinAlign + piece * VEC) *
+                                   C::ES;
+                    } else {
+                        boff[it] = 0x80000000u;
+                    }
+                }
             }
             blds[it] = (r * BN + tc) * RSA + piece * VEC;
         }
@@ -414,8 +435,12 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
             }
         // the chunk's channel block (a column tile's rows of one block are
         // contiguous) and its offset inside the block
-        const uint32_t bchunk = uniform(((cbase / kCinAlign) * (uint32_t)(a.C_out * T) * kCinAlign +
-                                         cbase % kCinAlign) * C::ES);
+        uint32_t bchunk;
+        if constexpr (DIL)  // (the packed weight's taps, not the kernel's)
+            bchunk = uniform((cbase / kCinAlign) * a.pw_cblock + (cbase % kCinAlign) * C::ES);
+        else
+            bchunk = uniform(((cbase / kCinAlign) * (uint32_t)(a.C_out * T) * kCinAlign +
+                              cbase % kCinAlign) * C::ES);
 #pragma unroll
         for (int it = 0; it < C::BITEMS; ++it)
             br[it] = __builtin_bit_cast(
@@ -862,7 +887,8 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
 
     S* __restrict__ yg = static_cast<S*>(a.y);
     const int nrows = a.TCO * R;
-    const bool vec_ok = (SS % VEC) == 0 && !a.atomic_out;
+    // (a dilation-reduced problem writes every g-th output: element stores)
+    const bool vec_ok = (SS % VEC) == 0 && !a.atomic_out && (!DIL || (a.gx == 1 && a.gy == 1));
     if (vec_ok && !a.phase_subset) {
         // Flattened over the tile: chunk e (VEC elements) is row e / cpr,
         // column chunk e % cpr of the staged output, so consecutive lanes
@@ -925,7 +951,10 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
             if (oy >= a.Ho || ox0 >= a.Wo) continue;
             lim = (int)min((int64_t)SS, a.Wo - ox0);
         }
-        const int64_t gbase = ((n * a.C_out + co) * a.Ho + oy) * a.Wo + ox0;
+        // staged (reduced) row -> real output row o0 + g * index per dimension
+        const int64_t gbase =
+            DIL ? ((n * a.C_out + co) * a.HoR + (a.o0y + a.gy * oy)) * a.WoR + a.o0x + a.gx * ox0
+                : ((n * a.C_out + co) * a.Ho + oy) * a.Wo + ox0;
         const S* srow = smem + co_l * CSTR + rr * SS;
         if (vec_ok) {
             for (int s0 = lane * VEC; s0 < lim; s0 += 64 * VEC) {
@@ -936,11 +965,22 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                 }
             }
         } else {
-            for (int e = lane; e < lim; e += 64) {
-                if (a.atomic_out)
-                    atomicAdd(reinterpret_cast<float*>(yg) + gbase + e, TR::to_f32(srow[e]));
-                else
-                    yg[gbase + e] = srow[e];
+            if (!DIL || a.gx == 1) {
+                for (int e = lane; e < lim; e += 64) {
+                    if (a.atomic_out)
+                        atomicAdd(reinterpret_cast<float*>(yg) + gbase + e, TR::to_f32(srow[e]));
+                    else
+                        yg[gbase + e] = srow[e];
+                }
+            } else if constexpr (DIL) {
+                // every gx-th output of the real row (dilation-reduced problem)
+                S* yrow = yg + gbase;
+                for (int e = lane; e < lim; e += 64) {
+                    if (a.atomic_out)
+                        atomicAdd(reinterpret_cast<float*>(yrow) + e * a.gx, TR::to_f32(srow[e]));
+                    else
+                        yrow[e * a.gx] = srow[e];
+                }
             }
         }
     }
@@ -955,14 +995,15 @@ using KernelFn = void (*)(const PolyArgs);
 struct Inst {
     KernelFn fn;
     int BM, BN, TAX, TAY, KC, threads, lds_bytes;
+    bool dil;  // runs dilation-reduced problems
 };
 
 template <class TR, int MY, int MX, int TAX, int RB, int CB, int WM, int WN, int KS,
-          bool XODD = false>
+          bool XODD = false, bool DIL = false>
 Inst make_inst() {
     using C = Cfg<TR, MY, MX, TAX, RB, CB, WM, WN, KS>;
-    return Inst{&poly_kernel<TR, MY, MX, TAX, RB, CB, WM, WN, KS, XODD>, C::BM, C::BN, TAX, C::TAY,
-                C::KC, C::NT, (int)(C::SMEM * C::ES)};
+    return Inst{&poly_kernel<TR, MY, MX, TAX, RB, CB, WM, WN, KS, XODD, DIL>, C::BM, C::BN, TAX,
+                C::TAY, C::KC, C::NT, (int)(C::SMEM * C::ES), DIL};
 }
 
 // Tile shapes.  16-bit storage, 1-D with one or two taps: 128 output rows x
@@ -1034,6 +1075,13 @@ bool pick_inst_x(const Problem& p, int CB, Inst* out) {
     if (p.mH == 1 && p.mW == 2) { *out = inst_2d<TR, 1, 2, XO>(); return true; }
     if (p.mH == 2 && p.mW == 1) { *out = inst_2d<TR, 2, 1, XO>(); return true; }
     if (p.mH == 2 && p.mW == 2) { *out = inst_2d<TR, 2, 2, XO>(); return true; }
+    // 3 x 3 taps (a 3 x 3 kernel at stride 1: dilation 2 at stride 2):
+    // 128 x 64 tiles, eight waves of 64 x 16, so that two stages of nine
+    // taps' weight rows fit in LDS
+    if (p.mH == 3 && p.mW == 3) {
+        *out = make_inst<TR, 3, 3, 32, 4, 1, 2, 4, 1, XO, true>();
+        return true;
+    }
     return false;
 }
 
@@ -1059,7 +1107,7 @@ bool get_inst(const Problem& p, int CB, Inst* out) {
 constexpr int64_t kInt32Max = 2147483647;
 
 // Fill PolyArgs for problem p; false when no kernel instance covers it.
-bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
+bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
     if (p.dH != 1 || p.dW != 1) return false;
     if (p.H == 0 || p.W == 0 || p.N == 0) return false;
     // every staged x load covers 8 bytes of one input row
@@ -1205,6 +1253,70 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
     return true;
 }
 
+// Dilation d dividing s, per dimension.  Output o receives a tap only when
+// o + p is a multiple of d (i*s - p + t*d = o with d | s); those outputs,
+// u = (o + p) / d, form the transposed convolution with stride s / d,
+// dilation 1 and the same taps.  Counting them from the first one,
+// o0 = (d - p mod d) mod d, gives u' = (o - o0) / d and left padding
+// u0 = (o0 + p) / d.  Without dilation the problem is returned unchanged.
+bool reduce_dilation(const Problem& p, Problem* q, int* o0y, int* o0x) {
+    *q = p;
+    *o0y = 0;
+    *o0x = 0;
+    auto one = [](int64_t d, int64_t s, int64_t pad, int64_t L, int64_t k, int64_t* s2,
+                  int64_t* pad2, int64_t* L2, int64_t* m2, int* o0) {
+        if (d == 1) return true;
+        if (d < 1 || s % d != 0) return false;
+        const int64_t first = (d - pad % d) % d;
+        *o0 = (int)first;
+        *s2 = s / d;
+        *pad2 = (first + pad) / d;
+        *L2 = L > first ? (L - first + d - 1) / d : 0;
+        *m2 = (k + *s2 - 1) / *s2;
+        return true;
+    };
+    if (!one(p.dH, p.sH, p.pH, p.Ho, p.kH, &q->sH, &q->pH, &q->Ho, &q->mH, o0y)) return false;
+    if (!one(p.dW, p.sW, p.pW, p.Wo, p.kW, &q->sW, &q->pW, &q->Wo, &q->mW, o0x)) return false;
+    q->dH = q->dW = 1;
+    q->opH = q->opW = 0;  // the reduced output sizes are set directly
+    q->P = q->sH * q->sW;
+    q->T = q->mH * q->mW;
+    return true;
+}
+
+// Fill PolyArgs for problem p (any dilation that divides the stride).
+bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
+    Problem q;
+    int o0y = 0, o0x = 0;
+    if (!reduce_dilation(p, &q, &o0y, &o0x)) return false;
+    if (q.Ho == 0 || q.Wo == 0) return false;
+    if (!plan_core(q, a, inst, splits)) return false;
+    // dilation is compiled into the 3 x 3-tap 2-D instances only
+    if ((p.dH > 1 || p.dW > 1) && !inst->dil) return false;
+    // the packed weight is the real one: its size, strides and taps
+    const int64_t pw_bytes = p.P * p.C_out * p.T * p.C_in_pad * (p.dtype == CTCONV_F32 ? 4 : 2);
+    // (an offset of 2^31 must lie past it: taps past k read as zero)
+    if (pw_bytes >= (int64_t)0x80000000LL) return false;
+    if (p.Ho > kInt32Max / 2 || p.Wo > kInt32Max / 2) return false;
+    a->pw_bytes = (uint32_t)pw_bytes;
+    a->gy = (int)p.dH;
+    a->gx = (int)p.dW;
+    a->o0y = o0y;
+    a->o0x = o0x;
+    a->HoR = p.Ho;
+    a->WoR = p.Wo;
+    a->psy = (int)p.sH;
+    a->psx = (int)p.sW;
+    a->pmx = (int)p.mW;
+    a->pT = (int)p.T;
+    a->pw_cblock = (uint32_t)(p.C_out * p.T * kCinAlign * (p.dtype == CTCONV_F32 ? 4 : 2));
+    a->kH = (int)p.kH;
+    a->kW = (int)p.kW;
+    a->fd_psy = make_fastdiv((uint32_t)p.sH);
+    a->fd_psx = make_fastdiv((uint32_t)p.sW);
+    return true;
+}
+
 }  // namespace
 
 bool polyphase_supported(const Problem& p) {
@@ -1224,7 +1336,9 @@ hipError_t launch_polyphase(const Problem& p, const void* x, const void* pw, con
     a.pw = pw;
     a.bias = bias;
     a.y = y;
-    if (a.atomic_out) {
+    // outputs no tap reaches (every one but each d-th under dilation) and
+    // the split-over-C_in accumulation start from the bias
+    if (a.atomic_out || a.gy > 1 || a.gx > 1) {
         const hipError_t e = launch_fill(p, bias, y, s);
         if (e != hipSuccess) return e;
     }
