@@ -21,11 +21,16 @@
  *    being zero in the packed weight, and output_padding only lengthens the
  *    output, so this route takes every shape with dilation 1.  It runs as an
  *    implicit GEMM on the MFMA matrix cores with the interleave, slice and
- *    bias fused into its epilogue, for m <= 4 (1-D) or m <= 2 per dimension
- *    (2-D) and input rows of at least 8 bytes (W >= 4 for bf16/fp16, W >= 2
- *    for fp32).
- *  - gather: every other shape (dilation, more taps, shorter rows), one
- *    output at a time from the tap condition.
+ *    bias fused into its epilogue, for m <= 4 (1-D), m <= 2 or m = 3 per
+ *    dimension (2-D: 1x1, 1x2, 2x1, 2x2 or 3x3 taps) and input rows of at
+ *    least 8 bytes (W >= 4 for bf16/fp16, W >= 2 for fp32).  In 2-D a
+ *    dilation d that divides the stride is taken too: only outputs o with
+ *    o + p divisible by d receive taps, and they form the transposed
+ *    convolution with stride s / d and dilation 1 over (o - o0) / d; when
+ *    that reduced problem has 3x3 taps (e.g. k = 3, s = d = 2) it runs on
+ *    this route after a bias fill of the other outputs.
+ *  - gather: every other shape (other dilations, more taps, shorter rows),
+ *    one output at a time from the tap condition.
  *
  * Layouts.  x [N, C_in, L] or [N, C_in, H, W]; y [N, C_out, L_out] or
  * [N, C_out, H_out, W_out]; bias [C_out]; all dense row-major (contiguous).
