@@ -1012,21 +1012,10 @@ Inst make_inst() {
 // the other's chunk loop; three or four taps: 256 rows, eight waves, one
 // workgroup per CU; 2-D: 4 x 64 rows x 128 columns, eight waves of 64 x 64.
 // fp32: 128 x 128 with eight waves of 64 x 32.
-#ifndef CTCONV_TILE_VARIANT
-#define CTCONV_TILE_VARIANT 2
-#endif
 template <class TR, int MY, int MX, int CB, bool XO>
 Inst inst_1d() {
     if constexpr (sizeof(typename TR::storage) == 2) {
-        if constexpr (CTCONV_TILE_VARIANT == 1)
-            return make_inst<TR, MY, MX, 128, 4, CB, 2, 2, 1, XO>();
-        else if constexpr (CTCONV_TILE_VARIANT == 3)
-            return make_inst<TR, MY, MX, 256, 8, (CB == 5 ? 5 : (MY * MX <= 2 ? 8 : 4)), 2, 2, 1, XO>();
-        else if constexpr (CTCONV_TILE_VARIANT == 4 && CB == 4 && MY * MX <= 2)
-            return make_inst<TR, MY, MX, 256, 4, 4, 4, 2, 2, XO>();
-        else if constexpr (CTCONV_TILE_VARIANT == 5 && CB == 4 && MY * MX <= 2)
-            return make_inst<TR, MY, MX, 256, 4, 8, 4, 2, 1, XO>();
-        else if constexpr (MY * MX <= 2)
+        if constexpr (MY * MX <= 2)
             return make_inst<TR, MY, MX, 128, 4, CB, 2, 2, 1, XO>();
         else
             // three or four taps: a 4-wave tile would stage twice the weight
@@ -1040,12 +1029,7 @@ Inst inst_1d() {
 template <class TR, int MY, int MX, bool XO>
 Inst inst_2d() {
     if constexpr (sizeof(typename TR::storage) == 2) {
-        if constexpr (CTCONV_TILE_VARIANT == 1)
-            return make_inst<TR, MY, MX, 32, 4, 4, 2, 2, 1, XO>();
-        else if constexpr (CTCONV_TILE_VARIANT == 3)
-            return make_inst<TR, MY, MX, 64, 8, (MY * MX <= 2 ? 8 : 4), 2, 2, 1, XO>();
-        else
-            return make_inst<TR, MY, MX, 64, 4, 4, 4, 2, 1, XO>();
+        return make_inst<TR, MY, MX, 64, 4, 4, 4, 2, 1, XO>();
     } else {
         return make_inst<TR, MY, MX, 32, 4, 2, 2, 4, 1, XO>();
     }
