@@ -814,7 +814,6 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                 const bool pair = first && pb + 1 < a.PT && bx + 1 < a.sx;
                 if (second && (pb - 1) - (int)fdiv((uint32_t)(pb - 1), a.fd_sx) * a.sx + 1 < a.sx)
                     continue;  // written together with the previous phase's block
-                const int co = co0 + co_l;
                 const float bv = bvs[cb];
                 // element offsets: lane part + wave-uniform part
                 const int lane_base = co_l * CSTR + lg * 4 * a.sx;
@@ -857,7 +856,6 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                 const int tc = bcol + cb * 16;
                 const int pb = (int)fdiv((uint32_t)tc, a.fd_tco), co_l = tc - pb * a.TCO;
                 if (pb >= a.PT) continue;
-                const int co = co0 + co_l;
                 const float bv = bvs[cb];
                 const int by = (int)fdiv((uint32_t)pb, a.fd_sx), bx = pb - by * a.sx;
         #pragma unroll
