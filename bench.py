@@ -53,6 +53,10 @@ def parse():
                     help="batch items of the workload in the oracle's timed sample")
     ap.add_argument("--cpu-frames", type=int, default=0,
                     help="leading input frames per item in the sample (0: all)")
+    ap.add_argument("--stream-frames", type=int, default=0,
+                    help="also time a streaming decode (N = 1) of the 1-D stack with this many "
+                         "input frames per call (12 frames = 80 ms of 24 kHz audio for the "
+                         "vocoder stack) and report it under \"stream\"")
     return ap.parse_args()
 
 
@@ -135,6 +139,64 @@ def cpu_baseline(wl, items, frames):
                       f"layer(s){' with ELU between' if wl.elu_between else ''}; "
                       f"{flops / 1e9:.2f} GFLOP in {dt:.2f} s, single-threaded float64",
             "seconds": dt, "host_nproc": os.cpu_count()}
+
+
+def stream_latency(wl, geo, packed, biases, args, C, dcode, tdt, fuse):
+    """Streaming decode at N = 1 (ctconv_stream_step per layer, each layer's
+    emitted outputs feeding the next): time per call of F input frames.
+    Each layer runs with padding 0 (the padded stack trims p outputs at the
+    two ends of the whole stream, which does not change the work)."""
+    import torch
+
+    F = args.stream_frames
+    if len(geo[0][1]) != 1 or any(g[0].kernel[0] < g[0].stride[0] for g in geo):
+        return {"error": "streaming needs a 1-D stack with k >= s"}
+    stream = torch.cuda.current_stream()
+    sptr = int(stream.cuda_stream)
+    C_in0 = geo[0][0].C_in
+    x = torch.randn((1, C_in0, F), device="cuda").to(tdt)
+    plan = []
+    L = F
+    cur = x
+    for li, (Ly_, sp, osp, _, _) in enumerate(geo):
+        Lr = geo[li][0]
+        k, s = Lr.kernel[0], Lr.stride[0]
+        Ly, Tl, ws_bytes = C.ctconv_stream_sizes(1, Lr.C_out, L, k, s, dcode)
+        y = torch.empty((1, Lr.C_out, Ly), dtype=tdt, device="cuda")
+        ws = torch.empty(ws_bytes // y.element_size() + 8, dtype=tdt, device="cuda")
+        tails = [torch.zeros((1, Lr.C_out, max(Tl, 1)), dtype=torch.float32, device="cuda")
+                 for _ in range(2)]
+        act = C.ACT_ELU if (fuse and li + 1 < len(geo)) else C.ACT_NONE
+        b = biases[li]
+        plan.append((cur, packed[li], b, y, tails, ws, Lr.C_in, Lr.C_out, L, k, s, Tl, act))
+        cur = y
+        L = Ly
+    fn = C.load().ctconv_stream_step
+    flip = [0]
+
+    def call():
+        for (xin, pw, b, y, tails, ws, ci, co, Lc, k, s, Tl, act) in plan:
+            tin, tout = tails[flip[0]], tails[1 - flip[0]]
+            st = fn(xin.data_ptr(), pw.data_ptr(), None if b is None else b.data_ptr(),
+                    y.data_ptr(), tin.data_ptr() if Tl > 0 else None,
+                    tout.data_ptr() if Tl > 0 else None, ws.data_ptr(), 1, ci, co, Lc, k, s,
+                    dcode, act, sptr)
+            assert st == 0, st
+        flip[0] ^= 1
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    calls = max(args.steps, 20)
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        call()
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / calls * 1e6
+    out_per_call = plan[-1][3].shape[2]
+    return {"N": 1, "frames_per_call": F, "outputs_per_call": int(out_per_call),
+            "calls": calls, "us_per_call": round(us, 2),
+            "launches_per_call": 2 * len(plan)}
 
 
 def main():
@@ -307,6 +369,8 @@ def main():
         "elu_us": [round(v * 1e3, 2) for v in elu_ms],
         "gflop_per_step": round(total_flops / 1e9, 3),
     }
+    if args.stream_frames > 0:
+        res["stream"] = stream_latency(wl, geo, packed, biases, args, C, dcode, tdt, fuse)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         res["cpu_baseline"] = cpu_baseline(wl, args.cpu_items, args.cpu_frames)

@@ -199,6 +199,59 @@ ctconv_status ctconv_query_route(int64_t N, int64_t C_in, int64_t C_out, int ndi
  */
 ctconv_status ctconv_elu(const void* x, void* y, int64_t n, ctconv_dtype dtype, void* stream);
 
+/*
+ * Streaming 1-D transposed convolution (padding 0, dilation 1, k >= s), for
+ * decoders that turn input frames into output samples chunk by chunk: the
+ * Phonon TTS example of ExecuTorch PR #25037 decodes one 80 ms frame per
+ * call through a StreamingConvTranspose1d that holds back the outputs later
+ * frames still add to, and uses the bias for the conv and for that held-back
+ * tail (the page's use-after-free fix).  Frame i reaches outputs
+ * [i*s, i*s + k), so after frames [0, F) the outputs below F*s are final and
+ * the next k - s are partial.
+ *
+ * Concatenating the y of successive ctconv_stream_step calls and then the y
+ * of ctconv_stream_flush gives the one-shot transposed convolution of all the
+ * frames with padding 0 (length (F - 1)*s + k), with the bias and the
+ * activation applied once to every output.  The tail is kept as fp32 partial
+ * sums without bias; products are accumulated in fp32 within a chunk, and a
+ * chunk's conv output is rounded to dtype once before the tail is added.
+ *
+ * ctconv_stream_sizes (host only): for a chunk of L_chunk frames, *y_len =
+ * L_chunk * s outputs per row, *tail_len = k - s (0 if k <= s) tail values per
+ * row, *workspace_bytes = N * C_out * (L_chunk*s + tail_len) * sizeof(dtype)
+ * for the chunk's conv output (0 when L_chunk = 0).
+ *
+ * ctconv_stream_step: one chunk.
+ *   x          device [N, C_in, L_chunk], L_chunk >= 1 frames
+ *   packed_w   from ctconv_prepack with kernel = k, stride = s (1-D)
+ *   bias       device [C_out] or NULL
+ *   y          device [N, C_out, L_chunk*s]: the outputs this chunk completes
+ *   tail_in    device fp32 [N, C_out, k - s] from the previous call, or NULL
+ *              at the start of the stream (zeros)
+ *   tail_out   device fp32 [N, C_out, k - s] (may be NULL when k = s); must
+ *              not be tail_in (pass two buffers and swap them per call)
+ *   workspace  device, ctconv_stream_sizes' workspace_bytes, caller-owned
+ *   act        activation applied to every emitted output (not to the tail)
+ * Errors: CTCONV_ERR_PARAM for k < s, tail_in == tail_out or an unknown act;
+ * CTCONV_ERR_SHAPE for L_chunk < 1; otherwise as ctconv_forward.  All
+ * buffers 16-byte aligned and caller-owned; nothing is retained.
+ *
+ * ctconv_stream_flush: the end of the stream, y [N, C_out, k - s] =
+ * act(tail_in + bias) (tail_in NULL: act(bias)).  Nothing is enqueued when
+ * k <= s or N = 0.
+ */
+ctconv_status ctconv_stream_sizes(int64_t N, int64_t C_out, int64_t L_chunk, int64_t kernel,
+                                  int64_t stride, ctconv_dtype dtype, int64_t* y_len,
+                                  int64_t* tail_len, int64_t* workspace_bytes);
+ctconv_status ctconv_stream_step(const void* x, const void* packed_w, const void* bias, void* y,
+                                 const float* tail_in, float* tail_out, void* workspace,
+                                 int64_t N, int64_t C_in, int64_t C_out, int64_t L_chunk,
+                                 int64_t kernel, int64_t stride, ctconv_dtype dtype,
+                                 ctconv_activation act, void* stream);
+ctconv_status ctconv_stream_flush(const float* tail_in, const void* bias, void* y, int64_t N,
+                                  int64_t C_out, int64_t kernel, int64_t stride,
+                                  ctconv_dtype dtype, ctconv_activation act, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

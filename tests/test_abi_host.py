@@ -206,3 +206,29 @@ def test_route_short_rows(lib, sp, dt, route):
     # shorter than that go to the gather kernel
     k, s, p = ((8,), (4,), (2,)) if len(sp) == 1 else ((4, 4), (2, 2), (1, 1))
     assert C.ctconv_query_route(2, 16, 16, sp, k, s, p, 0, 1, dt) == route
+
+
+def test_stream_sizes(lib):
+    # chunk of L frames: L*s outputs, k - s tail values, conv workspace
+    assert C.ctconv_stream_sizes(2, 3, 5, 10, 5, 1) == (25, 5, 2 * 3 * 30 * 2)
+    assert C.ctconv_stream_sizes(1, 4, 2, 16, 4, 0) == (8, 12, 1 * 4 * 20 * 4)
+    assert C.ctconv_stream_sizes(1, 4, 3, 4, 4, 2) == (12, 0, 1 * 4 * 12 * 2)
+    assert C.ctconv_stream_sizes(1, 4, 0, 8, 4, 1) == (0, 4, 0)
+
+
+def test_stream_validation_before_launch(lib):
+    # every call below returns before any launch (fake device pointers)
+    def step(k=8, s=4, L=3, tin=0x5000, tout=0x6000, act=0, ws=0x7000, N=1):
+        return lib.ctconv_stream_step(0x1000, 0x2000, None, 0x3000, tin, tout, ws, N, 4, 4, L, k,
+                                      s, 0, act, None)
+
+    assert step(k=3, s=4) == 3            # kernel shorter than stride
+    assert step(L=0) == 2                 # empty chunk
+    assert step(tin=0x5000, tout=0x5000) == 3  # tail buffers alias
+    assert step(act=7) == 3               # unknown activation
+    assert step(ws=None) == 1             # no workspace
+    assert step(tout=None) == 1           # tail needed (k > s)
+    assert step(N=0) == 0                 # nothing to do
+    assert lib.ctconv_stream_flush(0x5000, None, 0x3000, 1, 4, 8, 4, 0, 7, None) == 3
+    assert lib.ctconv_stream_flush(0x5000, None, 0x3000, 0, 4, 8, 4, 0, 0, None) == 0
+    assert lib.ctconv_stream_flush(0x5000, None, 0x3000, 1, 4, 4, 4, 0, 0, None) == 0  # no tail

@@ -1,0 +1,111 @@
+"""GPU: the streaming entry points (ctconv_stream_step / ctconv_stream_flush)
+through the C ABI.  Concatenating the outputs of the chunk calls and of the
+flush must equal the one-shot transposed convolution of all the frames with
+padding 0, computed by the CPU oracle on the same storage-rounded inputs,
+with the bias and the activation applied exactly once per output."""
+
+import numpy as np
+import pytest
+
+from synth import inputs as I
+
+from gpu_util import TOL, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cc():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    from vision_upsampler_decoders_amd import ctconv
+
+    ctconv.load()
+    return ctconv
+
+
+def _stream(cc, x, pw, b, C_out, k, s, chunks, act):
+    """Run the stream over x [N, C_in, F] in chunks of the given frame counts."""
+    import torch
+
+    N, C_in, F = x.shape
+    assert sum(chunks) == F
+    dt = cc.dtype_code(x)
+    stream = torch.cuda.current_stream().cuda_stream
+    _, Tl, _ = cc.ctconv_stream_sizes(N, C_out, 1, k, s, dt)
+    tails = [torch.empty((N, C_out, max(Tl, 1)), dtype=torch.float32, device="cuda")
+             for _ in range(2)]
+    tail_in = None
+    outs = []
+    f0 = 0
+    for i, L in enumerate(chunks):
+        Ly, Tl, ws_bytes = cc.ctconv_stream_sizes(N, C_out, L, k, s, dt)
+        xc = x[:, :, f0:f0 + L].contiguous()
+        y = torch.empty((N, C_out, Ly), dtype=x.dtype, device="cuda")
+        ws = torch.empty(ws_bytes // x.element_size() + 8, dtype=x.dtype, device="cuda")
+        tail_out = tails[i % 2]
+        cc.ctconv_stream_step(xc.data_ptr(), pw.data_ptr(), None if b is None else b.data_ptr(),
+                              y.data_ptr(), None if tail_in is None else tail_in.data_ptr(),
+                              tail_out.data_ptr() if Tl > 0 else None, ws.data_ptr(), N, C_in,
+                              C_out, L, k, s, dt, act, stream)
+        outs.append(y)
+        tail_in = tail_out if Tl > 0 else None
+        f0 += L
+    if Tl > 0:
+        y = torch.empty((N, C_out, Tl), dtype=x.dtype, device="cuda")
+        cc.ctconv_stream_flush(tail_in.data_ptr(), None if b is None else b.data_ptr(),
+                               y.data_ptr(), N, C_out, k, s, dt, act, stream)
+        outs.append(y)
+    torch.cuda.synchronize()
+    return torch.cat(outs, dim=2)
+
+
+STREAM_CASES = [
+    # name, dt, N, C_in, C_out, k, s, chunks, bias, act
+    ("k2s_bf16", "bf16", 2, 64, 48, 10, 5, (3, 1, 4, 2), True, 0),
+    # tail (12) longer than a one-frame chunk's output (4): carried over
+    ("long_tail_f32_elu", "f32", 1, 40, 24, 16, 4, (1, 1, 2, 5), True, 1),
+    ("k2s_f16_nobias", "f16", 2, 32, 16, 8, 4, (5, 7), False, 0),
+    ("k_eq_s_bf16", "bf16", 1, 48, 32, 4, 4, (2, 3), True, 0),
+    # the first vocoder layer's channels, one 8-frame chunk after another
+    ("voc_l0_bf16_elu", "bf16", 1, 512, 256, 16, 8, (8, 8, 8), True, 1),
+]
+
+
+@pytest.mark.parametrize("case", STREAM_CASES, ids=[c[0] for c in STREAM_CASES])
+def test_stream_equals_one_shot(cc, case):
+    from oracle import conv_transpose, elu as oelu, rel_l2
+
+    name, dt, N, C_in, C_out, k, s, chunks, has_b, act = case
+    say(f"stream {name}: chunks {chunks}")
+    F = sum(chunks)
+    seed = 800 + len(name)
+    x64 = I.normal(seed, (N, C_in, F), 1.0, dt)
+    w64 = I.normal(seed + 1, (C_in, C_out, k), (C_in * k) ** -0.5, dt)
+    b64 = I.uniform(seed + 2, (C_out,), -0.5, 0.5, dt) if has_b else None
+    pw = cc.prepack(to_dev(w64, dt), (s,))
+    y = _stream(cc, to_dev(x64, dt), pw, None if b64 is None else to_dev(b64, dt), C_out, k, s,
+                chunks, act)
+    ref = conv_transpose(x64, w64, b64, (s,), (0,))
+    if act == 1:
+        ref = oelu(ref)
+    assert tuple(y.shape) == ref.shape
+    err = rel_l2(to_host(y), ref)
+    say(f"  rel_l2 = {err:.3e}")
+    assert err <= TOL[dt], err
+
+
+def test_stream_bias_applied_once(cc):
+    """Zero frames: every emitted output, including those that pass through
+    the held-back tail, is exactly the bias (fp32)."""
+    import torch
+
+    N, C_in, C_out, k, s = 2, 16, 8, 12, 4
+    b64 = I.uniform(5, (C_out,), -1.0, 1.0, "f32")
+    w64 = I.normal(6, (C_in, C_out, k), 0.2, "f32")
+    x = torch.zeros((N, C_in, 7), dtype=torch.float32, device="cuda")
+    pw = cc.prepack(to_dev(w64, "f32"), (s,))
+    y = _stream(cc, x, pw, to_dev(b64, "f32"), C_out, k, s, (1, 2, 4), 0)
+    ref = np.broadcast_to(b64.astype(np.float32)[None, :, None], tuple(y.shape))
+    np.testing.assert_array_equal(to_host(y).astype(np.float32), ref)

@@ -29,7 +29,8 @@ FLAGS = [
     "-Wall", "-Wno-unused-function", "-Wno-unused-command-line-argument",
 ]
 
-SOURCES = ["ctconv_api.hip", "prepack.hip", "gather.hip", "pointwise.hip", "polyphase.hip"]
+SOURCES = ["ctconv_api.hip", "prepack.hip", "gather.hip", "pointwise.hip", "stream.hip",
+           "polyphase.hip"]
 
 
 def _compile(src: str) -> str:

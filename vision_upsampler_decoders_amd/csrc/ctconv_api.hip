@@ -266,6 +266,81 @@ ctconv_status ctconv_forward(const void* x, const void* packed_w, const void* bi
                                 CTCONV_ROUTE_AUTO, stream);
 }
 
+// Streaming geometry: emitted outputs per chunk (L * s), tail length
+// (k - s, or 0 when k <= s) and the chunk's full output length L*s + tail.
+namespace {
+ctconv_status stream_geometry(int64_t N, int64_t C_out, int64_t L, int64_t k, int64_t s,
+                              ctconv_dtype dt, int64_t* Ly, int64_t* Tl, int64_t* ws_bytes) {
+    if (!dtype_ok(dt)) return CTCONV_ERR_DTYPE;
+    if (k < 1 || s < 1) return CTCONV_ERR_PARAM;
+    if (N < 0 || C_out < 1 || L < 0) return CTCONV_ERR_SHAPE;
+    int64_t ly, t;
+    if (!mul_ok(L, s, &ly)) return CTCONV_ERR_SHAPE;
+    const int64_t tl = k > s ? k - s : 0;
+    if (ly > kI64Max - tl) return CTCONV_ERR_SHAPE;
+    if (!mul_ok(N, C_out, &t) || !mul_ok(t, ly + tl, &t) || !mul_ok(t, (int64_t)esize(dt), &t))
+        return CTCONV_ERR_SHAPE;
+    *Ly = ly;
+    *Tl = tl;
+    *ws_bytes = (L > 0 && k >= s) ? t : 0;
+    return CTCONV_OK;
+}
+}  // namespace
+
+ctconv_status ctconv_stream_sizes(int64_t N, int64_t C_out, int64_t L_chunk, int64_t kernel,
+                                  int64_t stride, ctconv_dtype dtype, int64_t* y_len,
+                                  int64_t* tail_len, int64_t* workspace_bytes) {
+    if (!y_len || !tail_len || !workspace_bytes) return CTCONV_ERR_NULL;
+    return stream_geometry(N, C_out, L_chunk, kernel, stride, dtype, y_len, tail_len,
+                           workspace_bytes);
+}
+
+ctconv_status ctconv_stream_step(const void* x, const void* packed_w, const void* bias, void* y,
+                                 const float* tail_in, float* tail_out, void* workspace,
+                                 int64_t N, int64_t C_in, int64_t C_out, int64_t L_chunk,
+                                 int64_t kernel, int64_t stride, ctconv_dtype dtype,
+                                 ctconv_activation act, void* stream) {
+    if (act != CTCONV_ACT_NONE && act != CTCONV_ACT_ELU) return CTCONV_ERR_PARAM;
+    int64_t Ly, Tl, ws;
+    ctconv_status st = stream_geometry(N, C_out, L_chunk, kernel, stride, dtype, &Ly, &Tl, &ws);
+    if (st != CTCONV_OK) return st;
+    // a kernel shorter than its stride leaves gaps between frames: not a stream of this form
+    if (kernel < stride) return CTCONV_ERR_PARAM;
+    if (L_chunk < 1) return CTCONV_ERR_SHAPE;
+    if (C_in < 1) return CTCONV_ERR_SHAPE;
+    if (N == 0) return CTCONV_OK;
+    if (!x || !packed_w || !y || !workspace || (Tl > 0 && !tail_out)) return CTCONV_ERR_NULL;
+    if (tail_in != nullptr && tail_in == tail_out) return CTCONV_ERR_PARAM;  // must not alias
+    if (!aligned16(x) || !aligned16(packed_w) || !aligned16(y) || !aligned16(workspace) ||
+        (bias && !aligned16(bias)) || (tail_in && !aligned16(tail_in)) ||
+        (tail_out && !aligned16(tail_out)))
+        return CTCONV_ERR_ALIGN;
+    // z = convT(chunk) with padding 0 and no bias, into the workspace
+    const int64_t one = 1, zero = 0;
+    st = ctconv_forward_act(x, packed_w, nullptr, workspace, N, C_in, C_out, 1, &L_chunk, &kernel,
+                            &stride, &zero, &zero, &one, dtype, CTCONV_ACT_NONE,
+                            CTCONV_ROUTE_AUTO, stream);
+    if (st != CTCONV_OK) return st;
+    return to_status(launch_stream_overlap(workspace, tail_in, bias, y, tail_out, N * C_out, C_out,
+                                           Ly, Tl, dtype, (int)act,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+ctconv_status ctconv_stream_flush(const float* tail_in, const void* bias, void* y, int64_t N,
+                                  int64_t C_out, int64_t kernel, int64_t stride,
+                                  ctconv_dtype dtype, ctconv_activation act, void* stream) {
+    if (act != CTCONV_ACT_NONE && act != CTCONV_ACT_ELU) return CTCONV_ERR_PARAM;
+    int64_t Ly, Tl, ws;
+    const ctconv_status st = stream_geometry(N, C_out, 0, kernel, stride, dtype, &Ly, &Tl, &ws);
+    if (st != CTCONV_OK) return st;
+    if (N == 0 || Tl == 0) return CTCONV_OK;
+    if (!y) return CTCONV_ERR_NULL;
+    if (!aligned16(y) || (bias && !aligned16(bias)) || (tail_in && !aligned16(tail_in)))
+        return CTCONV_ERR_ALIGN;
+    return to_status(launch_stream_flush(tail_in, bias, y, N * C_out, C_out, Tl, dtype, (int)act,
+                                         static_cast<hipStream_t>(stream)));
+}
+
 ctconv_status ctconv_elu(const void* x, void* y, int64_t n, ctconv_dtype dtype, void* stream) {
     if (!x || !y) return CTCONV_ERR_NULL;
     if (!dtype_ok(dtype)) return CTCONV_ERR_DTYPE;

@@ -169,6 +169,15 @@ hipError_t launch_gather(const Problem& p, const void* x, const void* pw, const 
 hipError_t launch_fill(const Problem& p, const void* bias, void* y, hipStream_t s);
 hipError_t launch_elu(const void* x, void* y, int64_t n, ctconv_dtype dt, hipStream_t s);
 
+// Streaming overlap-add and flush (rows = N * C_out; Ly emitted outputs and
+// Tl tail values per row).
+hipError_t launch_stream_overlap(const void* z, const float* tail_in, const void* bias, void* y,
+                                 float* tail_out, int64_t rows, int64_t C_out, int64_t Ly,
+                                 int64_t Tl, ctconv_dtype dt, int act, hipStream_t s);
+hipError_t launch_stream_flush(const float* tail_in, const void* bias, void* y, int64_t rows,
+                               int64_t C_out, int64_t Tl, ctconv_dtype dt, int act,
+                               hipStream_t s);
+
 // Polyphase planning and launch.  plan_polyphase returns false when no
 // compiled kernel instance covers the shape.
 bool polyphase_supported(const Problem& p);

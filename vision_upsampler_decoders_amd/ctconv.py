@@ -22,7 +22,8 @@ STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_PARAM", 4: "ERR_DTYPE"
 EXPORTED = (
     "ctconv_abi_version", "ctconv_status_string", "ctconv_output_shape", "ctconv_packed_bytes",
     "ctconv_prepack", "ctconv_forward", "ctconv_forward_route", "ctconv_forward_act",
-    "ctconv_query_route", "ctconv_elu",
+    "ctconv_query_route", "ctconv_elu", "ctconv_stream_sizes", "ctconv_stream_step",
+    "ctconv_stream_flush",
 )
 
 ACT_NONE, ACT_ELU = 0, 1
@@ -72,6 +73,14 @@ def load(path: str = LIB_PATH):
     lib.ctconv_query_route.restype = c_int
     lib.ctconv_elu.argtypes = [c_vp, c_vp, c_i64, c_int, c_vp]
     lib.ctconv_elu.restype = c_int
+    lib.ctconv_stream_sizes.argtypes = [c_i64, c_i64, c_i64, c_i64, c_i64, c_int, _i64p, _i64p,
+                                        _i64p]
+    lib.ctconv_stream_sizes.restype = c_int
+    lib.ctconv_stream_step.argtypes = [c_vp] * 7 + [c_i64] * 6 + [c_int, c_int, c_vp]
+    lib.ctconv_stream_step.restype = c_int
+    lib.ctconv_stream_flush.argtypes = [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_int,
+                                        c_int, c_vp]
+    lib.ctconv_stream_flush.restype = c_int
     _lib = lib
     return lib
 
@@ -190,6 +199,33 @@ def ctconv_query_route(N: int, C_in: int, C_out: int, in_spatial, kernel, stride
 
 def ctconv_elu(x_ptr: int, y_ptr: int, n: int, dtype: int, stream: int) -> None:
     _check("ctconv_elu", load().ctconv_elu(x_ptr, y_ptr, n, dtype, stream))
+
+
+def ctconv_stream_sizes(N: int, C_out: int, L_chunk: int, kernel: int, stride: int,
+                        dtype: int) -> Tuple[int, int, int]:
+    a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check("ctconv_stream_sizes",
+           load().ctconv_stream_sizes(N, C_out, L_chunk, kernel, stride, dtype, ctypes.byref(a),
+                                      ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
+def ctconv_stream_step(x_ptr: int, packed_ptr: int, bias_ptr: Optional[int], y_ptr: int,
+                       tail_in_ptr: Optional[int], tail_out_ptr: Optional[int], ws_ptr: int, N: int,
+                       C_in: int, C_out: int, L_chunk: int, kernel: int, stride: int, dtype: int,
+                       act: int, stream: int) -> None:
+    _check("ctconv_stream_step",
+           load().ctconv_stream_step(x_ptr, packed_ptr, bias_ptr, y_ptr, tail_in_ptr,
+                                     tail_out_ptr, ws_ptr, N, C_in, C_out, L_chunk, kernel,
+                                     stride, dtype, act, stream))
+
+
+def ctconv_stream_flush(tail_in_ptr: Optional[int], bias_ptr: Optional[int], y_ptr: int, N: int,
+                        C_out: int, kernel: int, stride: int, dtype: int, act: int,
+                        stream: int) -> None:
+    _check("ctconv_stream_flush",
+           load().ctconv_stream_flush(tail_in_ptr, bias_ptr, y_ptr, N, C_out, kernel, stride,
+                                      dtype, act, stream))
 
 
 # ---------------------------------------------------------------------------
