@@ -172,31 +172,52 @@ def stream_latency(wl, geo, packed, biases, args, C, dcode, tdt, fuse):
         cur = y
         L = Ly
     fn = C.load().ctconv_stream_step
-    flip = [0]
 
-    def call():
+    def call(parity):
+        # launches go to the current stream (the capture stream inside a graph)
+        sp = int(torch.cuda.current_stream().cuda_stream)
         for (xin, pw, b, y, tails, ws, ci, co, Lc, k, s, Tl, act) in plan:
-            tin, tout = tails[flip[0]], tails[1 - flip[0]]
+            tin, tout = tails[parity], tails[1 - parity]
             st = fn(xin.data_ptr(), pw.data_ptr(), None if b is None else b.data_ptr(),
                     y.data_ptr(), tin.data_ptr() if Tl > 0 else None,
                     tout.data_ptr() if Tl > 0 else None, ws.data_ptr(), 1, ci, co, Lc, k, s,
-                    dcode, act, sptr)
+                    dcode, act, sp)
             assert st == 0, st
-        flip[0] ^= 1
 
-    for _ in range(args.warmup):
-        call()
+    calls = max(args.steps, 20) // 2 * 2
+    for i in range(args.warmup * 2):
+        call(i % 2)
     torch.cuda.synchronize()
-    calls = max(args.steps, 20)
     t0 = time.perf_counter()
-    for _ in range(calls):
-        call()
+    for i in range(calls):
+        call(i % 2)
     torch.cuda.synchronize()
     us = (time.perf_counter() - t0) / calls * 1e6
+    # the same two calls (the tails alternate) captured once as a HIP graph
+    # and replayed: one launch of the graph instead of 12 kernel launches
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(0)
+        call(1)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        call(0)
+        call(1)
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(calls // 2):
+        g.replay()
+    torch.cuda.synchronize()
+    us_graph = (time.perf_counter() - t0) / calls * 1e6
     out_per_call = plan[-1][3].shape[2]
     return {"N": 1, "frames_per_call": F, "outputs_per_call": int(out_per_call),
             "calls": calls, "us_per_call": round(us, 2),
-            "launches_per_call": 2 * len(plan)}
+            "us_per_call_graph": round(us_graph, 2), "launches_per_call": 2 * len(plan)}
 
 
 def main():
