@@ -200,6 +200,25 @@ ctconv_status ctconv_query_route(int64_t N, int64_t C_in, int64_t C_out, int ndi
 ctconv_status ctconv_elu(const void* x, void* y, int64_t n, ctconv_dtype dtype, void* stream);
 
 /*
+ * The iSTFT steps after the overlap-add.  onnxruntime PR #33978 ("[WebGPU]
+ * optimizations for audio models") serves the iSTFT's inverse DFT and
+ * overlap-add with ConvTranspose; the window-square normalisation and the
+ * centre trim come after it.  With y [rows, L_in] the overlap-added frames
+ * (ctconv_forward of the Hann-windowed inverse-DFT basis, stride hop) and
+ * env [L_in] the window-square envelope sum_f h^2[t - f*hop] (itself a
+ * transposed convolution of a row of ones with h^2, stride hop):
+ *   out[r, t] = y[r, trim + t] / env[trim + t]   for t < L_out
+ * (0 where env <= 1e-11: no frame covers the sample).  For a centred STFT,
+ * trim = n_fft / 2 and L_out = hop * (frames - 1).  Computed in fp32,
+ * rounded once to dtype; all three buffers of dtype, 16-byte aligned, on the
+ * device, caller-owned; out must not overlap y or env.  CTCONV_ERR_SHAPE
+ * when trim + L_out > L_in.
+ */
+ctconv_status ctconv_istft_normalize(const void* y, const void* env, void* out, int64_t rows,
+                                     int64_t L_in, int64_t trim, int64_t L_out,
+                                     ctconv_dtype dtype, void* stream);
+
+/*
  * Streaming 1-D transposed convolution (padding 0, dilation 1, k >= s), for
  * decoders that turn input frames into output samples chunk by chunk: the
  * Phonon TTS example of ExecuTorch PR #25037 decodes one 80 ms frame per

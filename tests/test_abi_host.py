@@ -232,3 +232,13 @@ def test_stream_validation_before_launch(lib):
     assert lib.ctconv_stream_flush(0x5000, None, 0x3000, 1, 4, 8, 4, 0, 7, None) == 3
     assert lib.ctconv_stream_flush(0x5000, None, 0x3000, 0, 4, 8, 4, 0, 0, None) == 0
     assert lib.ctconv_stream_flush(0x5000, None, 0x3000, 1, 4, 4, 4, 0, 0, None) == 0  # no tail
+
+
+def test_istft_normalize_validation(lib):
+    f = lib.ctconv_istft_normalize
+    assert f(0x1000, 0x2000, 0x3000, 2, 100, 60, 41, 0, None) == 2   # trim + L_out > L_in
+    assert f(0x1000, 0x2000, 0x3000, 2, 100, -1, 10, 0, None) == 2
+    assert f(None, 0x2000, 0x3000, 2, 100, 10, 10, 0, None) == 1
+    assert f(0x1001, 0x2000, 0x3000, 2, 100, 10, 10, 0, None) == 5
+    assert f(0x1000, 0x2000, 0x3000, 2, 100, 10, 10, 9, None) == 4
+    assert f(0x1000, 0x2000, 0x3000, 0, 100, 10, 10, 0, None) == 0   # nothing to do

@@ -169,3 +169,41 @@ def test_stream_steps_in_a_graph_match_eager(cc):
         for q in range(2):
             assert torch.equal(ys[q], ref[2 * j + q]), (j, q)
         say(f"graph replay {j}: equal to eager")
+
+
+@pytest.mark.parametrize("n_fft,hop,T", [(256, 64, 20), (512, 128, 9)])
+def test_istft_pipeline_matches_torch_istft(cc, n_fft, hop, T):
+    """Inverse DFT + overlap-add as ctconv_forward with the Hann-windowed
+    basis, the window-square envelope as ctconv_forward of ones with h^2,
+    then ctconv_istft_normalize (trim n_fft/2, hop*(T-1) samples): equal to
+    torch.istft (centred, periodic Hann, float64 on the CPU, an independent
+    library routine) within the fp32 bar."""
+    import torch
+
+    from oracle import rel_l2
+
+    N, F = 2, n_fft // 2 + 1
+    rng = np.random.default_rng(n_fft + T)
+    X = rng.standard_normal((N, F, T)) + 1j * rng.standard_normal((N, F, T))
+    x64 = I.round_to_dtype(np.concatenate([X.real, X.imag], axis=1), "f32")
+    Xr = x64[:, :F] + 1j * x64[:, F:]
+    w = to_dev(I.istft_basis(n_fft, "f32"), "f32")
+    pw = cc.prepack(w, (hop,))
+    y = cc.forward(to_dev(x64, "f32"), pw, None, 1, (n_fft,), (hop,))
+    h = I.hann_periodic(n_fft)
+    wsq = to_dev(I.round_to_dtype((h * h).reshape(1, 1, n_fft), "f32"), "f32")
+    env = cc.forward(torch.ones((1, 1, T), dtype=torch.float32, device="cuda"),
+                     cc.prepack(wsq, (hop,)), None, 1, (n_fft,), (hop,))
+    L_in = y.shape[2]
+    trim, L_out = n_fft // 2, hop * (T - 1)
+    out = torch.empty((N, L_out), dtype=torch.float32, device="cuda")
+    cc.ctconv_istft_normalize(y.data_ptr(), env.data_ptr(), out.data_ptr(), N, L_in, trim, L_out,
+                              0, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ref = torch.istft(torch.from_numpy(Xr), n_fft, hop_length=hop,
+                      window=torch.hann_window(n_fft, periodic=True, dtype=torch.float64),
+                      center=True, normalized=False, onesided=True).numpy()
+    assert ref.shape == (N, L_out)
+    err = rel_l2(to_host(out), ref)
+    say(f"istft n_fft={n_fft} hop={hop} T={T}: rel_l2 = {err:.3e}")
+    assert err <= 1e-5, err

@@ -341,6 +341,21 @@ ctconv_status ctconv_stream_flush(const float* tail_in, const void* bias, void* 
                                          static_cast<hipStream_t>(stream)));
 }
 
+ctconv_status ctconv_istft_normalize(const void* y, const void* env, void* out, int64_t rows,
+                                     int64_t L_in, int64_t trim, int64_t L_out,
+                                     ctconv_dtype dtype, void* stream) {
+    if (!dtype_ok(dtype)) return CTCONV_ERR_DTYPE;
+    if (rows < 0 || L_in < 0 || trim < 0 || L_out < 0) return CTCONV_ERR_SHAPE;
+    if (trim > L_in || L_out > L_in - trim) return CTCONV_ERR_SHAPE;
+    int64_t t;
+    if (!mul_ok(rows, L_in, &t) || !mul_ok(t, (int64_t)esize(dtype), &t)) return CTCONV_ERR_SHAPE;
+    if (rows == 0 || L_out == 0) return CTCONV_OK;
+    if (!y || !env || !out) return CTCONV_ERR_NULL;
+    if (!aligned16(y) || !aligned16(env) || !aligned16(out)) return CTCONV_ERR_ALIGN;
+    return to_status(launch_istft_norm(y, env, out, rows, L_in, trim, L_out, dtype,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 ctconv_status ctconv_elu(const void* x, void* y, int64_t n, ctconv_dtype dtype, void* stream) {
     if (!x || !y) return CTCONV_ERR_NULL;
     if (!dtype_ok(dtype)) return CTCONV_ERR_DTYPE;

@@ -168,6 +168,9 @@ hipError_t launch_gather(const Problem& p, const void* x, const void* pw, const 
                          void* y, hipStream_t s);
 hipError_t launch_fill(const Problem& p, const void* bias, void* y, hipStream_t s);
 hipError_t launch_elu(const void* x, void* y, int64_t n, ctconv_dtype dt, hipStream_t s);
+hipError_t launch_istft_norm(const void* y, const void* env, void* out, int64_t rows,
+                             int64_t L_in, int64_t trim, int64_t L_out, ctconv_dtype dt,
+                             hipStream_t s);
 
 // Streaming overlap-add and flush (rows = N * C_out; Ly emitted outputs and
 // Tl tail values per row).

@@ -1,4 +1,4 @@
-// Bias fill and ELU.
+// Bias fill, ELU and the iSTFT tail (window-envelope normalisation and trim).
 //
 // fill: every output element gets bias[co] (or 0).  It serves outputs no tap
 // reaches -- an empty input with a non-empty output, the case onnxruntime PR
@@ -54,6 +54,24 @@ __global__ __launch_bounds__(256) void elu_kernel_v8(const uint4* x, uint4* y, i
     }
 }
 
+// iSTFT tail: out[r, t] = y[r, trim + t] / env[trim + t] (0 where the
+// window-square envelope env is below 1e-11, i.e. no frame covers the sample).
+template <class TR>
+__global__ __launch_bounds__(256) void istft_norm_kernel(const typename TR::storage* __restrict__ y,
+                                                         const typename TR::storage* __restrict__ env,
+                                                         typename TR::storage* __restrict__ out,
+                                                         int64_t rows, int64_t L_in, int64_t trim,
+                                                         int64_t L_out) {
+    const int64_t total = rows * L_out;
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t r = i / L_out, t = i - r * L_out;
+        const float e = TR::to_f32(env[trim + t]);
+        const float v = TR::to_f32(y[r * L_in + trim + t]);
+        out[i] = TR::from_f32(e > 1e-11f ? v / e : 0.f);
+    }
+}
+
 int64_t grid_for(int64_t work) {
     int64_t b = (work + 255) / 256;
     if (b > 65536) b = 65536;
@@ -89,7 +107,29 @@ hipError_t elu_t(const void* x, void* y, int64_t n, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <class TR>
+hipError_t istft_norm_t(const void* y, const void* env, void* out, int64_t rows, int64_t L_in,
+                        int64_t trim, int64_t L_out, hipStream_t s) {
+    using S = typename TR::storage;
+    istft_norm_kernel<TR><<<dim3((unsigned)grid_for(rows * L_out)), dim3(256), 0, s>>>(
+        static_cast<const S*>(y), static_cast<const S*>(env), static_cast<S*>(out), rows, L_in,
+        trim, L_out);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_istft_norm(const void* y, const void* env, void* out, int64_t rows,
+                             int64_t L_in, int64_t trim, int64_t L_out, ctconv_dtype dt,
+                             hipStream_t s) {
+    if (rows * L_out <= 0) return hipSuccess;
+    switch (dt) {
+        case CTCONV_F32: return istft_norm_t<TF32>(y, env, out, rows, L_in, trim, L_out, s);
+        case CTCONV_BF16: return istft_norm_t<TBF16>(y, env, out, rows, L_in, trim, L_out, s);
+        case CTCONV_F16: return istft_norm_t<TF16>(y, env, out, rows, L_in, trim, L_out, s);
+    }
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_fill(const Problem& p, const void* bias, void* y, hipStream_t s) {
     switch (p.dtype) {

@@ -23,7 +23,7 @@ EXPORTED = (
     "ctconv_abi_version", "ctconv_status_string", "ctconv_output_shape", "ctconv_packed_bytes",
     "ctconv_prepack", "ctconv_forward", "ctconv_forward_route", "ctconv_forward_act",
     "ctconv_query_route", "ctconv_elu", "ctconv_stream_sizes", "ctconv_stream_step",
-    "ctconv_stream_flush",
+    "ctconv_stream_flush", "ctconv_istft_normalize",
 )
 
 ACT_NONE, ACT_ELU = 0, 1
@@ -81,6 +81,9 @@ def load(path: str = LIB_PATH):
     lib.ctconv_stream_flush.argtypes = [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_int,
                                         c_int, c_vp]
     lib.ctconv_stream_flush.restype = c_int
+    lib.ctconv_istft_normalize.argtypes = [c_vp, c_vp, c_vp, c_i64, c_i64, c_i64, c_i64, c_int,
+                                           c_vp]
+    lib.ctconv_istft_normalize.restype = c_int
     _lib = lib
     return lib
 
@@ -226,6 +229,13 @@ def ctconv_stream_flush(tail_in_ptr: Optional[int], bias_ptr: Optional[int], y_p
     _check("ctconv_stream_flush",
            load().ctconv_stream_flush(tail_in_ptr, bias_ptr, y_ptr, N, C_out, kernel, stride,
                                       dtype, act, stream))
+
+
+def ctconv_istft_normalize(y_ptr: int, env_ptr: int, out_ptr: int, rows: int, L_in: int,
+                           trim: int, L_out: int, dtype: int, stream: int) -> None:
+    _check("ctconv_istft_normalize",
+           load().ctconv_istft_normalize(y_ptr, env_ptr, out_ptr, rows, L_in, trim, L_out, dtype,
+                                         stream))
 
 
 # ---------------------------------------------------------------------------
