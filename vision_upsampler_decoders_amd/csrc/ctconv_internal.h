@@ -111,7 +111,7 @@ inline FastDiv make_fastdiv(uint32_t d) {
     return FastDiv{(uint32_t)((pw + d - 1) / d), s};
 }
 
-__device__ inline uint32_t fdiv(uint32_t n, FastDiv f) {
+__host__ __device__ inline uint32_t fdiv(uint32_t n, FastDiv f) {
     return (uint32_t)(((uint64_t)n * f.m) >> f.s);
 }
 
