@@ -557,7 +557,6 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     // once when they fit in registers), then for each class present the A
     // fragments of all taps, then that class's MFMAs.
     constexpr bool Y2 = C::TAY > 1;  // 2-D tile: the row offset may differ too
-    constexpr bool BPRE = CB * T <= 8;
     int cls[CB];
     uint32_t clsmask = 0;
 #pragma unroll
@@ -571,22 +570,18 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int kofs = ks * C::KSTEP + lg * VEC;
-            u32x4 bpre[BPRE ? CB : 1][BPRE ? T : 1];
-            if constexpr (BPRE) {
+            // one tap at a time: its CB B fragments once, then per shift class
+            // present its RB A fragments and the MFMAs of that class's blocks
+#pragma unroll
+            for (int r = 0; r < T; ++r) {
+                u32x4 bfr[CB];
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb)
+                    bfr[cb] = *reinterpret_cast<const u32x4*>(
+                        bs + (r * BN + bcol + cb * 16) * RSA + kofs);
 #pragma unroll
-                    for (int r = 0; r < T; ++r)
-                        bpre[cb][r] = *reinterpret_cast<const u32x4*>(
-                            bs + (r * BN + bcol + cb * 16) * RSA + kofs);
-            }
-#pragma unroll
-            for (int c = 0; c < (Y2 ? 4 : 2); ++c) {
-                if (!(clsmask & (1u << c))) continue;
-                // one tap at a time: its RB A fragments, its CB B fragments,
-                // then the MFMAs of the column blocks in this class
-#pragma unroll
-                for (int r = 0; r < T; ++r) {
+                for (int c = 0; c < (Y2 ? 4 : 2); ++c) {
+                    if (!(clsmask & (1u << c))) continue;
                     const int ey = (c >> 1) + MY - 1 - r / MX;
                     const int ex = (c & 1) + MX - 1 - r % MX;
                     u32x4 afr[RB];
@@ -594,15 +589,6 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                     for (int rb = 0; rb < RB; ++rb)
                         afr[rb] = *reinterpret_cast<const u32x4*>(
                             xs + (arow[rb] + ey * WXP + ex) * RSA + kofs);
-                    u32x4 bfr[CB];
-#pragma unroll
-                    for (int cb = 0; cb < CB; ++cb) {
-                        if constexpr (BPRE)
-                            bfr[cb] = bpre[cb][r];
-                        else
-                            bfr[cb] = *reinterpret_cast<const u32x4*>(
-                                bs + (r * BN + bcol + cb * 16) * RSA + kofs);
-                    }
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb)
                         if (cls[cb] == c) {
