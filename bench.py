@@ -32,7 +32,13 @@ sys.path.insert(0, ROOT)
 METRIC = "ConvTranspose TFLOP/s (2*N*Cin*Cout*K*Lin) and % of MFMA/HBM roofline, 1 GPU"
 PEAK_MFMA = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # dense TFLOP/s
 PEAK_HBM = 8000.0  # GB/s
+FLUSH_BYTES = 512 << 20  # larger than the 256 MB MALL
 ESIZE = {"f32": 4, "bf16": 2, "f16": 2}
+
+
+def pcts(ms_samples):
+    """p10, median and p90 of per-launch durations (ms in, us out)."""
+    return [round(float(v) * 1e3, 2) for v in np.percentile(ms_samples, [10, 50, 90])]
 
 
 def log(msg):
@@ -46,6 +52,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="vocoder_stack")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-reps", type=int, default=20,
+                    help="steps timed after a 512 MiB cache flush (at most --steps)")
     ap.add_argument("--separate-elu", action="store_true",
                     help="run the ELU between layers as its own pass instead of fusing it "
                          "into the producing layer's epilogue")
@@ -315,8 +323,28 @@ def main():
     for k in range(args.steps):
         step(evs[k])
     torch.cuda.synchronize()
-    layer_ms = [float(np.mean([evs[k][li][0].elapsed_time(evs[k][li][1])
-                               for k in range(args.steps)])) for li in range(n_layers)]
+    layer_samples = [[evs[k][li][0].elapsed_time(evs[k][li][1]) for k in range(args.steps)]
+                     for li in range(n_layers)]
+    layer_ms = [float(np.mean(v)) for v in layer_samples]
+
+    # cold regime: before each step, overwrite a 512 MiB buffer on the same stream so that
+    # neither L2 nor the 256 MB MALL still holds the step's inputs or weights
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    cold_reps = max(1, min(args.steps, args.cold_reps))
+    evc = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in range(2 * n_layers)] for _ in range(cold_reps)]
+    evs_step = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+                for _ in range(cold_reps)]
+    for k in range(cold_reps):
+        flush.fill_(float(k))
+        evs_step[k][0].record(stream)
+        step(evc[k])
+        evs_step[k][1].record(stream)
+    torch.cuda.synchronize()
+    del flush
+    cold_layer_samples = [[evc[k][li][0].elapsed_time(evc[k][li][1]) for k in range(cold_reps)]
+                          for li in range(n_layers)]
+    cold_step_ms = [evs_step[k][0].elapsed_time(evs_step[k][1]) for k in range(cold_reps)]
     elu_ms = [float(np.mean([evs[k][n_layers + li][0].elapsed_time(evs[k][n_layers + li][1])
                              for k in range(args.steps)]))
               for li in range(n_layers) if elus[li] is not None]
@@ -338,6 +366,8 @@ def main():
             "stride": list(L.stride), "in": list(sp), "out": list(osp),
             "route": {1: "polyphase", 2: "gather"}[route],
             "us": round(layer_ms[li] * 1e3, 2),
+            "us_p10_p50_p90": pcts(layer_samples[li]),
+            "us_cold_p10_p50_p90": pcts(cold_layer_samples[li]),
             "tflops": round(fl / t / 1e12, 2), "gbps": round(nb / t / 1e9, 1),
             "bound": "mfma" if t_mfma >= t_hbm else "hbm",
             "frac_roofline": round(max(t_mfma, t_hbm) / t, 4),
@@ -360,6 +390,12 @@ def main():
     roof["kernel"] = f"layer {dom} ({Ld['route']}), {Ld['C_in']}->{Ld['C_out']} k{Ld['kernel']} s{Ld['stride']}"
     roof["algorithmic_per_launch"] = {"flop": fl_d, "bytes": nb_d}
     roof["avg_launch_us"] = Ld["us"]
+    # the same launch after a cache flush (median over the cold reps)
+    t_c = float(np.median(cold_layer_samples[dom])) * 1e-3
+    ach_c = fl_d / t_c / 1e12 if roof["bound"] == "mfma" else nb_d / t_c / 1e9
+    roof["cold"] = {"achieved": round(ach_c, 2 if roof["bound"] == "mfma" else 1),
+                    "frac": round(ach_c / roof["peak"], 4), "median_launch_us": round(t_c * 1e6, 2),
+                    "reps": cold_reps}
 
     t_roof = sum(max(g[3] / (PEAK_MFMA[wl.dtype] * 1e12), g[4] / (PEAK_HBM * 1e9)) for g in geo)
 
@@ -386,6 +422,7 @@ def main():
                               for g in geo]},
         "roofline": roof,
         "step_roofline_fraction": round(t_roof / (ms_per_step * 1e-3), 4),
+        "ms_per_step_cold_p10_p50_p90": [round(v / 1e3, 4) for v in pcts(cold_step_ms)],
         "layers": layers,
         "elu_us": [round(v * 1e3, 2) for v in elu_ms],
         "gflop_per_step": round(total_flops / 1e9, 3),

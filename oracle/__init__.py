@@ -1,4 +1,4 @@
-"""CPU reference for dense transposed convolution (ConvTranspose1d/2d).
+"""CPU reference for transposed convolution (ConvTranspose1d/2d, dense and grouped).
 
 TEST INFRASTRUCTURE ONLY.  Only tests/, the smoke check in __graft_entry__ and
 the CPU-baseline leg of bench.py may import this package.  The GPU library
@@ -48,6 +48,11 @@ def _load():
             [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64] + [i64p] * 6 + [dp] * 4)
         lib.ctconv_oracle_points.argtypes = (
             [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64] + [i64p] * 6
+            + [dp] * 3 + [i64p, ctypes.c_int64, dp])
+        lib.ctconv_oracle_conv_transpose_grouped.argtypes = (
+            [ctypes.c_int] + [ctypes.c_int64] * 4 + [i64p] * 6 + [dp] * 4)
+        lib.ctconv_oracle_points_grouped.argtypes = (
+            [ctypes.c_int] + [ctypes.c_int64] * 4 + [i64p] * 6
             + [dp] * 3 + [i64p, ctypes.c_int64, dp])
         lib.ctconv_oracle_istft_ola.argtypes = [ctypes.c_int64] * 4 + [dp, dp]
         lib.ctconv_oracle_rfft.argtypes = [ctypes.c_int64, dp, dp, dp]
@@ -130,6 +135,54 @@ def conv_transpose_points(x, w, bias, idx, stride=1, padding=0, output_padding=0
     out = np.empty(idx.shape[0], dtype=np.float64)
     rc = _load().ctconv_oracle_points(
         ndim, N, C_in, C_out, _i64(x.shape[2:]), _i64(k), _i64(s), _i64(p), _i64(op),
+        _i64(d), _dp(x), _dp(w), _dp(b),
+        idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), idx.shape[0], _dp(out))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return out
+
+
+def conv_transpose_grouped(x, w, bias=None, groups=1, stride=1, padding=0, output_padding=0,
+                           dilation=1):
+    """Grouped ConvTranspose in float64 by the scatter definition.
+
+    x [N, C_in, *sp], w [C_in, C_out / groups, *k], bias [C_out] or None;
+    groups = C_in is the depthwise case.
+    """
+    x = _f64(x)
+    w = _f64(w)
+    b = None if bias is None else _f64(bias)
+    ndim = x.ndim - 2
+    N, C_in = x.shape[:2]
+    assert w.shape[0] == C_in and w.ndim == ndim + 2
+    C_out = w.shape[1] * groups
+    k = list(w.shape[2:])
+    s, p, op, d = (_per_dim(a, ndim) for a in (stride, padding, output_padding, dilation))
+    osp = output_shape(x.shape[2:], k, s, p, op, d)
+    y = np.empty((N, C_out) + osp, dtype=np.float64)
+    rc = _load().ctconv_oracle_conv_transpose_grouped(
+        ndim, N, C_in, C_out, groups, _i64(x.shape[2:]), _i64(k), _i64(s), _i64(p), _i64(op),
+        _i64(d), _dp(x), _dp(w), _dp(b), _dp(y))
+    if rc != 0:
+        raise ValueError("oracle rejected the arguments")
+    return y
+
+
+def conv_transpose_grouped_points(x, w, bias, idx, groups=1, stride=1, padding=0,
+                                  output_padding=0, dilation=1):
+    """Selected outputs of the grouped case; idx [P, 4] of (n, co, oy, ox) (1-D: oy = 0)."""
+    x = _f64(x)
+    w = _f64(w)
+    b = None if bias is None else _f64(bias)
+    ndim = x.ndim - 2
+    N, C_in = x.shape[:2]
+    C_out = w.shape[1] * groups
+    k = list(w.shape[2:])
+    s, p, op, d = (_per_dim(a, ndim) for a in (stride, padding, output_padding, dilation))
+    idx = np.ascontiguousarray(np.asarray(idx, dtype=np.int64).reshape(-1, 4))
+    out = np.empty(idx.shape[0], dtype=np.float64)
+    rc = _load().ctconv_oracle_points_grouped(
+        ndim, N, C_in, C_out, groups, _i64(x.shape[2:]), _i64(k), _i64(s), _i64(p), _i64(op),
         _i64(d), _dp(x), _dp(w), _dp(b),
         idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), idx.shape[0], _dp(out))
     if rc != 0:

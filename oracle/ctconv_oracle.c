@@ -182,6 +182,125 @@ int ctconv_oracle_points(int ndim, int64_t N, int64_t C_in, int64_t C_out,
     return OR_OK;
 }
 
+/*
+ * Grouped transposed convolution (the groups argument of ConvTranspose), same
+ * scatter definition.  The channels split into G equal groups: input channel
+ * ci lies in group g = ci / (C_in / G) and reaches only the output channels
+ * co = g * (C_out / G) + j, j < C_out / G, through w[ci, j, t]; the weight is
+ * [C_in, C_out / G, k...].  G = C_in is the depthwise transposed convolution
+ * (one input channel per group) that ExecuTorch PR #25037, commit
+ * "Decompose depthwise transposed convs", rewrites into per-phase depthwise
+ * stride-1 convolutions and a depth-to-space; G = 1 is the dense case above.
+ *   x    [N, C_in, H, W]            (1-D: [N, C_in, L])
+ *   w    [C_in, C_out/G, kH, kW]    (1-D: [C_in, C_out/G, k])
+ *   bias [C_out] or NULL
+ *   y    [N, C_out, Ho, Wo]         written completely
+ */
+int ctconv_oracle_conv_transpose_grouped(int ndim, int64_t N, int64_t C_in, int64_t C_out,
+                                         int64_t groups, const int64_t* in_sp,
+                                         const int64_t* kernel, const int64_t* stride,
+                                         const int64_t* padding, const int64_t* output_padding,
+                                         const int64_t* dilation, const double* x,
+                                         const double* w, const double* bias, double* y) {
+    int64_t in2[2], k2[2], s2[2], p2[2], op2[2], d2[2], o2[2];
+    if (or_expand(ndim, in_sp, 1, in2) || or_expand(ndim, kernel, 1, k2) ||
+        or_expand(ndim, stride, 1, s2) || or_expand(ndim, padding, 0, p2) ||
+        or_expand(ndim, output_padding, 0, op2) || or_expand(ndim, dilation, 1, d2))
+        return OR_BAD;
+    if (N < 0 || C_in < 1 || C_out < 1 || groups < 1 || C_in % groups || C_out % groups)
+        return OR_BAD;
+    for (int a = 0; a < 2; ++a) {
+        o2[a] = or_out_len(in2[a], k2[a], s2[a], p2[a], op2[a], d2[a]);
+        if (o2[a] < 1) return OR_BAD;
+    }
+    const int64_t H = in2[0], W = in2[1], Ho = o2[0], Wo = o2[1];
+    const int64_t kH = k2[0], kW = k2[1];
+    const int64_t cig = C_in / groups, cog = C_out / groups;
+
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t co = 0; co < C_out; ++co) {
+            double b = bias ? bias[co] : 0.0;
+            double* yp = y + (n * C_out + co) * Ho * Wo;
+            for (int64_t e = 0; e < Ho * Wo; ++e) yp[e] = b;
+        }
+
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t ci = 0; ci < C_in; ++ci) {
+            const int64_t g = ci / cig;
+            for (int64_t iy = 0; iy < H; ++iy)
+                for (int64_t ix = 0; ix < W; ++ix) {
+                    const double xv = x[((n * C_in + ci) * H + iy) * W + ix];
+                    for (int64_t j = 0; j < cog; ++j) {
+                        const int64_t co = g * cog + j;
+                        for (int64_t ty = 0; ty < kH; ++ty) {
+                            const int64_t oy = iy * s2[0] - p2[0] + ty * d2[0];
+                            if (oy < 0 || oy >= Ho) continue;
+                            for (int64_t tx = 0; tx < kW; ++tx) {
+                                const int64_t ox = ix * s2[1] - p2[1] + tx * d2[1];
+                                if (ox < 0 || ox >= Wo) continue;
+                                const double wv = w[((ci * cog + j) * kH + ty) * kW + tx];
+                                y[((n * C_out + co) * Ho + oy) * Wo + ox] += xv * wv;
+                            }
+                        }
+                    }
+                }
+        }
+    return OR_OK;
+}
+
+/*
+ * Selected outputs of the grouped transposed convolution, one at a time:
+ * output (n, co, oy, ox) collects the terms of the input channels of co's
+ * group, each input position solved from the tap as in ctconv_oracle_points.
+ *   idx  [n_pts][4] = (n, co, oy, ox); 1-D uses oy = 0.
+ */
+int ctconv_oracle_points_grouped(int ndim, int64_t N, int64_t C_in, int64_t C_out,
+                                 int64_t groups, const int64_t* in_sp, const int64_t* kernel,
+                                 const int64_t* stride, const int64_t* padding,
+                                 const int64_t* output_padding, const int64_t* dilation,
+                                 const double* x, const double* w, const double* bias,
+                                 const int64_t* idx, int64_t n_pts, double* out) {
+    int64_t in2[2], k2[2], s2[2], p2[2], op2[2], d2[2], o2[2];
+    if (or_expand(ndim, in_sp, 1, in2) || or_expand(ndim, kernel, 1, k2) ||
+        or_expand(ndim, stride, 1, s2) || or_expand(ndim, padding, 0, p2) ||
+        or_expand(ndim, output_padding, 0, op2) || or_expand(ndim, dilation, 1, d2))
+        return OR_BAD;
+    if (groups < 1 || C_in % groups || C_out % groups) return OR_BAD;
+    for (int a = 0; a < 2; ++a) {
+        o2[a] = or_out_len(in2[a], k2[a], s2[a], p2[a], op2[a], d2[a]);
+        if (o2[a] < 1) return OR_BAD;
+    }
+    const int64_t H = in2[0], W = in2[1];
+    const int64_t kH = k2[0], kW = k2[1];
+    const int64_t cig = C_in / groups, cog = C_out / groups;
+    for (int64_t e = 0; e < n_pts; ++e) {
+        const int64_t n = idx[4 * e], co = idx[4 * e + 1];
+        const int64_t oy = idx[4 * e + 2], ox = idx[4 * e + 3];
+        if (n < 0 || n >= N || co < 0 || co >= C_out || oy < 0 || oy >= o2[0] ||
+            ox < 0 || ox >= o2[1])
+            return OR_BAD;
+        const int64_t g = co / cog, j = co % cog;
+        double acc = bias ? bias[co] : 0.0;
+        for (int64_t ci = g * cig; ci < (g + 1) * cig; ++ci)
+            for (int64_t ty = 0; ty < kH; ++ty) {
+                const int64_t ny = oy + p2[0] - ty * d2[0];
+                if (ny < 0 || ny % s2[0] != 0) continue;
+                const int64_t iy = ny / s2[0];
+                if (iy >= H) continue;
+                for (int64_t tx = 0; tx < kW; ++tx) {
+                    const int64_t nx = ox + p2[1] - tx * d2[1];
+                    if (nx < 0 || nx % s2[1] != 0) continue;
+                    const int64_t ix = nx / s2[1];
+                    if (ix >= W) continue;
+                    acc += x[((n * C_in + ci) * H + iy) * W + ix] *
+                           w[((ci * cog + j) * kH + ty) * kW + tx];
+                }
+            }
+        out[e] = acc;
+    }
+    return OR_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Inverse STFT by overlap-add, independent of the transposed convolution.  */
 /* ------------------------------------------------------------------------ */

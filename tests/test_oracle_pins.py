@@ -13,6 +13,9 @@ Each check below is independent of the oracle's own loops:
     (tests/golden/hand_worked.json);
   * the inverse-STFT closed forms: numpy's irfft + Hann + overlap-add, and
     perfect reconstruction (periodic Hann squared at hop n/4 sums to 3/2);
+  * the grouped (depthwise) case: torch's grouped conv_transpose in float64,
+    the dense oracle on the block-diagonal expansion of the grouped weight, and
+    impulse responses that stay inside their channel group;
   * planted-mistake runs: copies of the oracle with one plausible bug each must
     fail these pins.
 """
@@ -349,6 +352,127 @@ def test_planted_mistakes_are_caught(oracle_mod, tmp_path, name, monkeypatch):
             caught = True
             break
         ref = _torch_ref(x, w, b, s, p, op, d)
+        if y.shape != ref.shape or not np.allclose(y, ref, rtol=1e-12, atol=1e-12):
+            caught = True
+            break
+    assert caught, f"mutation {name} was not detected"
+
+
+# --------------------------------------------------------------------------
+# grouped / depthwise transposed convolution (groups = C_in is depthwise)
+# --------------------------------------------------------------------------
+
+GROUPED_CASES = [
+    # (C_in, C_out, groups, spatial, k, s, p, op, d, bias)
+    (4, 4, 4, (9,), (4,), (2,), (1,), (0,), (1,), True),       # depthwise, k = 2s
+    (3, 6, 3, (7,), (6,), (3,), (2,), (1,), (1,), False),      # depthwise, multiplier 2
+    (4, 4, 4, (5,), (3,), (2,), (1,), (1,), (2,), True),       # dilation
+    (4, 6, 2, (6,), (5,), (2,), (1,), (0,), (1,), True),       # two groups
+    (3, 3, 3, (4, 5), (4, 4), (2, 2), (1, 1), (0, 0), (1, 1), True),
+    (2, 4, 2, (3, 4), (3, 3), (2, 2), (1, 1), (1, 1), (1, 1), False),
+    (2, 2, 2, (4, 3), (3, 3), (2, 2), (1, 1), (1, 1), (2, 2), True),
+    (2, 2, 2, (3, 5), (5, 2), (3, 1), (2, 0), (2, 0), (1, 1), True),
+]
+
+
+def _make_grouped(case, seed):
+    C_in, C_out, g, sp, k, s, p, op, d, has_b = case
+    x = _rand((2, C_in) + sp, seed)
+    w = _rand((C_in, C_out // g) + k, seed + 1)
+    b = _rand((C_out,), seed + 2) if has_b else None
+    return x, w, b, g, s, p, op, d
+
+
+def _torch_grouped(x, w, b, g, s, p, op, d):
+    fn = F.conv_transpose1d if x.ndim == 3 else F.conv_transpose2d
+    return fn(torch.from_numpy(x), torch.from_numpy(w),
+              None if b is None else torch.from_numpy(b), stride=s, padding=p,
+              output_padding=op, groups=g, dilation=d).numpy()
+
+
+@pytest.mark.parametrize("case", GROUPED_CASES)
+def test_grouped_vs_torch_float64(oracle_mod, case):
+    x, w, b, g, s, p, op, d = _make_grouped(case, 31)
+    y = oracle_mod.conv_transpose_grouped(x, w, b, g, s, p, op, d)
+    ref = _torch_grouped(x, w, b, g, s, p, op, d)
+    assert y.shape == ref.shape
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", GROUPED_CASES)
+def test_grouped_equals_dense_with_block_diagonal_weight(oracle_mod, case):
+    """A grouped weight is the dense weight that is zero between groups."""
+    x, w, b, g, s, p, op, d = _make_grouped(case, 41)
+    C_in, cog = w.shape[:2]
+    cig = C_in // g
+    dense = np.zeros((C_in, cog * g) + w.shape[2:])
+    for ci in range(C_in):
+        grp = ci // cig
+        dense[ci, grp * cog:(grp + 1) * cog] = w[ci]
+    y = oracle_mod.conv_transpose_grouped(x, w, b, g, s, p, op, d)
+    yd = oracle_mod.conv_transpose(x, dense, b, s, p, op, d)
+    np.testing.assert_allclose(y, yd, rtol=1e-13, atol=1e-13)
+
+
+def test_depthwise_impulse_response(oracle_mod):
+    """One input element of channel c reaches only channels c*M .. c*M + M-1,
+    at o = i*s - p + t*d, with the weights themselves."""
+    C, M, L, k, s, p = 3, 2, 6, 5, 2, 1
+    w = _rand((C, M, k), 7)
+    for c0, i0 in [(0, 0), (2, 5), (1, 3)]:
+        x = np.zeros((1, C, L))
+        x[0, c0, i0] = 1.0
+        y = oracle_mod.conv_transpose_grouped(x, w, None, C, s, p)
+        expect = np.zeros_like(y)
+        for j in range(M):
+            for t in range(k):
+                o = i0 * s - p + t
+                if 0 <= o < y.shape[2]:
+                    expect[0, c0 * M + j, o] = w[c0, j, t]
+        np.testing.assert_array_equal(y, expect)
+
+
+@pytest.mark.parametrize("case", [GROUPED_CASES[1], GROUPED_CASES[2], GROUPED_CASES[5],
+                                  GROUPED_CASES[7]])
+def test_grouped_points_match_full(oracle_mod, case):
+    x, w, b, g, s, p, op, d = _make_grouped(case, 51)
+    y = oracle_mod.conv_transpose_grouped(x, w, b, g, s, p, op, d)
+    rng = np.random.default_rng(3)
+    n = rng.integers(0, y.shape[0], 40)
+    co = rng.integers(0, y.shape[1], 40)
+    if y.ndim == 3:
+        oy = np.zeros(40, dtype=np.int64)
+        ox = rng.integers(0, y.shape[2], 40)
+        want = y[n, co, ox]
+    else:
+        oy = rng.integers(0, y.shape[2], 40)
+        ox = rng.integers(0, y.shape[3], 40)
+        want = y[n, co, oy, ox]
+    got = oracle_mod.conv_transpose_grouped_points(x, w, b, np.stack([n, co, oy, ox], 1), g,
+                                                   s, p, op, d)
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=1e-13)
+
+
+GROUPED_MUTATIONS = {
+    "group_of_channel": ("const int64_t g = ci / cig;", "const int64_t g = ci % groups;"),
+    "grouped_weight_index": ("const double wv = w[((ci * cog + j) * kH + ty) * kW + tx];",
+                             "const double wv = w[((j * C_in + ci) * kH + ty) * kW + tx];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GROUPED_MUTATIONS))
+def test_grouped_planted_mistakes_are_caught(oracle_mod, tmp_path, name, monkeypatch):
+    MUTATIONS_ALL = dict(MUTATIONS, **GROUPED_MUTATIONS)
+    monkeypatch.setitem(MUTATIONS, name, MUTATIONS_ALL[name])
+    so = _build_mutant(tmp_path, name)
+    monkeypatch.setattr(oracle_mod, "_lib", None)
+    monkeypatch.setattr(oracle_mod, "_LIB", so)
+    monkeypatch.setattr(oracle_mod, "build", lambda force=False: so)
+    caught = False
+    for case in GROUPED_CASES:
+        x, w, b, g, s, p, op, d = _make_grouped(case, 61)
+        y = oracle_mod.conv_transpose_grouped(x, w, b, g, s, p, op, d)
+        ref = _torch_grouped(x, w, b, g, s, p, op, d)
         if y.shape != ref.shape or not np.allclose(y, ref, rtol=1e-12, atol=1e-12):
             caught = True
             break
