@@ -79,8 +79,9 @@ def layer_geometry(wl):
         osp = C.ctconv_output_shape(sp, L.kernel, L.stride, L.padding, L.output_padding,
                                     L.dilation)
         K = int(np.prod(L.kernel))
-        flops = 2 * wl.N * L.C_in * L.C_out * K * int(np.prod(sp))
-        nbytes = es * (wl.N * L.C_in * int(np.prod(sp)) + L.C_in * L.C_out * K
+        cog = L.C_out // L.groups  # output channels per group (all of them when dense)
+        flops = 2 * wl.N * L.C_in * cog * K * int(np.prod(sp))
+        nbytes = es * (wl.N * L.C_in * int(np.prod(sp)) + L.C_in * cog * K
                        + (L.C_out if L.bias else 0) + wl.N * L.C_out * int(np.prod(osp)))
         out.append((L, sp, osp, flops, nbytes))
         sp = osp
@@ -136,9 +137,14 @@ def cpu_baseline(wl, items, frames):
     t0 = time.perf_counter()
     cur = x
     for li, L in enumerate(wl.layers):
-        flops += 2 * items * L.C_in * L.C_out * int(np.prod(L.kernel)) * int(np.prod(cur.shape[2:]))
-        cur = oracle.conv_transpose(cur, ws[li], bs[li], L.stride, L.padding,
-                                    L.output_padding, L.dilation)
+        flops += (2 * items * L.C_in * (L.C_out // L.groups) * int(np.prod(L.kernel))
+                  * int(np.prod(cur.shape[2:])))
+        if L.groups == 1:
+            cur = oracle.conv_transpose(cur, ws[li], bs[li], L.stride, L.padding,
+                                        L.output_padding, L.dilation)
+        else:
+            cur = oracle.conv_transpose_grouped(cur, ws[li], bs[li], L.groups, L.stride,
+                                                L.padding, L.output_padding, L.dilation)
         if wl.elu_between and li + 1 < len(wl.layers):
             cur = oracle.elu(cur)
     dt = time.perf_counter() - t0
@@ -259,7 +265,8 @@ def main():
     packed, biases, outs, elus = [], [], [], []
     for li, (L, sp, osp, _, _) in enumerate(geo):
         w = dev(I.gen_w(wl, li))
-        packed.append(C.prepack(w, L.stride))
+        # a depthwise layer reads its weight as is; a dense one its packed form
+        packed.append(w if L.groups > 1 else C.prepack(w, L.stride))
         b = I.gen_bias(wl, li)
         biases.append(None if b is None else dev(b))
         outs.append(torch.empty((wl.N, L.C_out) + osp, dtype=tdt, device="cuda"))
@@ -274,10 +281,12 @@ def main():
     n_layers = len(geo)
     # arguments marshalled once per layer: each launch is one foreign call
     fuse = wl.elu_between and not args.separate_elu
-    convs = [C.Conv(wl.N, L.C_in, L.C_out, sp, L.kernel, L.stride, L.padding, L.output_padding,
-                    L.dilation, dcode,
-                    act=C.ACT_ELU if (fuse and li + 1 < len(geo)) else C.ACT_NONE)
+    convs = [(C.DepthwiseConv if L.groups > 1 else C.Conv)(
+                 wl.N, L.C_in, L.C_out, sp, L.kernel, L.stride, L.padding, L.output_padding,
+                 L.dilation, dcode, act=C.ACT_ELU if (fuse and li + 1 < len(geo)) else C.ACT_NONE)
              for li, (L, sp, osp, _, _) in enumerate(geo)]
+    if any(L.groups not in (1, L.C_in) for L in wl.layers):
+        raise SystemExit("grouped layers other than depthwise (groups = C_in) are not built")
     ptrs = []
     cur_ptr = x.data_ptr()
     for li in range(n_layers):
@@ -356,15 +365,20 @@ def main():
     layers = []
     for li, (L, sp, osp, fl, nb) in enumerate(geo):
         t = layer_ms[li] * 1e-3
-        route = C.ctconv_query_route(wl.N, L.C_in, L.C_out, sp, L.kernel, L.stride, L.padding,
-                                     L.output_padding, L.dilation,
-                                     {"f32": 0, "bf16": 1, "f16": 2}[wl.dtype])
+        if L.groups > 1:
+            route = 10 + C.ctconv_depthwise_query_kernel(
+                wl.N, L.C_in, L.C_out, sp, L.kernel, L.stride, L.padding, L.output_padding,
+                L.dilation, dcode)
+        else:
+            route = C.ctconv_query_route(wl.N, L.C_in, L.C_out, sp, L.kernel, L.stride,
+                                         L.padding, L.output_padding, L.dilation, dcode)
         t_mfma = fl / (PEAK_MFMA[wl.dtype] * 1e12)
         t_hbm = nb / (PEAK_HBM * 1e9)
         layers.append({
             "layer": li, "C_in": L.C_in, "C_out": L.C_out, "kernel": list(L.kernel),
             "stride": list(L.stride), "in": list(sp), "out": list(osp),
-            "route": {1: "polyphase", 2: "gather"}[route],
+            "route": {1: "polyphase", 2: "gather", 11: "depthwise row-phase",
+                      12: "depthwise element"}[route],
             "us": round(layer_ms[li] * 1e3, 2),
             "us_p10_p50_p90": pcts(layer_samples[li]),
             "us_cold_p10_p50_p90": pcts(cold_layer_samples[li]),

@@ -1,6 +1,7 @@
 /*
  * ctconv.h -- dense transposed convolution (ConvTranspose1d/2d, groups = 1)
- * on AMD Instinct MI355X (gfx950).  C ABI.
+ * and depthwise transposed convolution (groups = C_in) on AMD Instinct MI355X
+ * (gfx950).  C ABI.
  *
  * Operation (scatter definition).  Every input element x[n, ci, i] adds
  * x[n, ci, i] * w[ci, co, t] to the output element at o = i*s - p + t*d for
@@ -270,6 +271,65 @@ ctconv_status ctconv_stream_step(const void* x, const void* packed_w, const void
 ctconv_status ctconv_stream_flush(const float* tail_in, const void* bias, void* y, int64_t N,
                                   int64_t C_out, int64_t kernel, int64_t stride,
                                   ctconv_dtype dtype, ctconv_activation act, void* stream);
+
+/* Kernel choice of the depthwise transposed convolution. */
+typedef enum {
+    CTCONV_DW_AUTO = 0,   /* row-phase kernel when it covers the shape, else element kernel */
+    CTCONV_DW_ROW = 1,    /* force the row-phase kernel (CTCONV_ERR_PARAM if it does not apply) */
+    CTCONV_DW_ELEMENT = 2 /* force the element kernel (valid for every shape) */
+} ctconv_dw_kernel;
+
+/*
+ * Depthwise transposed convolution: ConvTranspose with groups = C_in and
+ * C_out = M * C_in (M >= 1 outputs per input channel).  Output channel co
+ * reads input channel co / M only:
+ *     y[n, co, o] = bias[co] + sum_t x[n, co / M, i] * w[co / M, co % M, t]
+ * over the taps t and positions i with o = i*s - p + t*d (per dimension in
+ * 2-D), the scatter definition of ctconv_forward restricted to one channel.
+ * This is the depthwise layer (an upsampling filter applied per channel) that
+ * ExecuTorch PR #25037, commit "Decompose depthwise transposed convs",
+ * rewrites into one stride-1 depthwise convolution per output phase and a
+ * depth-to-space; here the phases are computed in place, each lane writing a
+ * run of consecutive (interleaved) outputs.
+ *   x      device [N, C_in, in_spatial...]; may be NULL when it has no element
+ *   w      device [C_in, M, kernel...], the ConvTranspose weight layout, used
+ *          as is (no prepack)
+ *   bias   device [C_out] or NULL
+ *   y      device [N, C_out, out_spatial...] (ctconv_output_shape), every
+ *          element written; must not overlap x, w or bias
+ *   act    activation applied after the bias, before the one rounding
+ * Products are accumulated in fp32 and rounded once to dtype.  Kernels: the
+ * row-phase kernel takes dilation 1, a last-dimension stride of 1, 2 or 4,
+ * an H stride (2-D) of at most 4, at most 4 taps per phase in each dimension
+ * (ceil(k / s) <= 4) and x below 2 GiB; the element kernel takes every other
+ * shape.
+ * Errors: as ctconv_forward, plus CTCONV_ERR_SHAPE when C_out is not a
+ * multiple of C_in, CTCONV_ERR_PARAM for an unknown act or kernel choice or a
+ * forced row-phase kernel that does not apply.  Pointers 16-byte aligned;
+ * asynchronous on `stream`; nothing is allocated or retained.
+ */
+ctconv_status ctconv_depthwise_forward(const void* x, const void* w, const void* bias, void* y,
+                                       int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                                       const int64_t* in_spatial, const int64_t* kernel,
+                                       const int64_t* stride, const int64_t* padding,
+                                       const int64_t* output_padding, const int64_t* dilation,
+                                       ctconv_dtype dtype, ctconv_activation act, void* stream);
+ctconv_status ctconv_depthwise_forward_kernel(const void* x, const void* w, const void* bias,
+                                              void* y, int64_t N, int64_t C_in, int64_t C_out,
+                                              int ndim, const int64_t* in_spatial,
+                                              const int64_t* kernel, const int64_t* stride,
+                                              const int64_t* padding,
+                                              const int64_t* output_padding,
+                                              const int64_t* dilation, ctconv_dtype dtype,
+                                              ctconv_activation act, ctconv_dw_kernel which,
+                                              void* stream);
+/* Which kernel CTCONV_DW_AUTO would run (host only; validates like the forward). */
+ctconv_status ctconv_depthwise_query_kernel(int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                                            const int64_t* in_spatial, const int64_t* kernel,
+                                            const int64_t* stride, const int64_t* padding,
+                                            const int64_t* output_padding,
+                                            const int64_t* dilation, ctconv_dtype dtype,
+                                            ctconv_dw_kernel* which);
 
 #ifdef __cplusplus
 }

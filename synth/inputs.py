@@ -117,6 +117,7 @@ class Layer:
     output_padding: Tuple[int, ...]
     dilation: Tuple[int, ...]
     bias: bool
+    groups: int = 1  # C_in for a depthwise layer (weight [C_in, C_out / groups, k...])
 
     @property
     def ndim(self) -> int:
@@ -138,9 +139,9 @@ class Workload:
     extra: Dict = field(default_factory=dict)
 
 
-def _L(C_in, C_out, k, s, p, op=0, d=1, bias=False, ndim=1):
+def _L(C_in, C_out, k, s, p, op=0, d=1, bias=False, ndim=1, groups=1):
     t = lambda v: tuple(v) if isinstance(v, (tuple, list)) else (v,) * ndim  # noqa: E731
-    return Layer(C_in, C_out, t(k), t(s), t(p), t(op), t(d), bias)
+    return Layer(C_in, C_out, t(k), t(s), t(p), t(op), t(d), bias, groups)
 
 
 WORKLOADS: Dict[str, Workload] = {
@@ -184,6 +185,20 @@ WORKLOADS: Dict[str, Workload] = {
         [_L(128, 64, 3, 2, 1, op=1, d=2, ndim=2)],
         ("uniform", -1.0, 1.0), "uniform",
         note="ConvTranspose2d fp32 128->64 3x3 s2 p1 op1 dilation 2, 96x96, N=4"),
+    # Depthwise (groups = C) 4x4 stride-2 upsampling filter per channel, the
+    # layer type of a StyleGAN-style x2 upsampler (MI-GAN has twelve of them).
+    "depthwise2d": Workload(
+        6, "depthwise2d", "bf16", 8, (128, 128),
+        [_L(256, 256, 4, 2, 1, bias=True, ndim=2, groups=256)],
+        ("normal", 1.0), "fan_in_normal",
+        note="depthwise ConvTranspose2d bf16 256 channels 4x4 s2 p1, 128x128, N=8, bias"),
+    # Depthwise k = 2s stride-2 upsampler along time (an audio decoder's
+    # frame-rate upsampler), long enough to stream well past the caches.
+    "depthwise1d": Workload(
+        7, "depthwise1d", "bf16", 8, (16384,),
+        [_L(512, 512, 4, 2, 1, groups=512)],
+        ("normal", 1.0), "fan_in_normal",
+        note="depthwise ConvTranspose1d bf16 512 channels k4 s2 p1, L_in=16384, N=8"),
 }
 
 
@@ -199,13 +214,14 @@ def gen_x(wl: Workload, N: Optional[int] = None, in_spatial=None) -> np.ndarray:
 
 def gen_w(wl: Workload, li: int = 0) -> np.ndarray:
     L = wl.layers[li]
-    shape = (L.C_in, L.C_out) + L.kernel
+    shape = (L.C_in, L.C_out // L.groups) + L.kernel
     seed = SEED(wl.wid, 2, li + 1 if len(wl.layers) > 1 else 0)
     if wl.w_dist == "uniform":
         return uniform(seed, shape, -1.0, 1.0, wl.dtype)
     if wl.w_dist == "fan_in_normal":
-        # N(0, v) with v = 1 / (C_in * prod(kernel)): the second parameter is the variance.
-        v = 1.0 / (L.C_in * int(np.prod(L.kernel)))
+        # N(0, v) with v = 1 / (fan-in * prod(kernel)): the second parameter is the
+        # variance; an output of a grouped layer sums C_in / groups input channels.
+        v = 1.0 / ((L.C_in // L.groups) * int(np.prod(L.kernel)))
         return normal(seed, shape, math.sqrt(v), wl.dtype)
     if wl.w_dist == "istft":
         return istft_basis(wl.extra["n_fft"], wl.dtype)
@@ -225,5 +241,5 @@ def workload(name: str) -> Workload:
 
 
 def flops(N: int, L: Layer, in_sp) -> int:
-    """2 * N * C_in * C_out * prod(kernel) * prod(in_spatial)."""
-    return 2 * N * L.C_in * L.C_out * int(np.prod(L.kernel)) * int(np.prod(in_sp))
+    """2 * N * C_in * (C_out / groups) * prod(kernel) * prod(in_spatial)."""
+    return 2 * N * L.C_in * (L.C_out // L.groups) * int(np.prod(L.kernel)) * int(np.prod(in_sp))

@@ -242,3 +242,55 @@ def test_istft_normalize_validation(lib):
     assert f(0x1001, 0x2000, 0x3000, 2, 100, 10, 10, 0, None) == 5
     assert f(0x1000, 0x2000, 0x3000, 2, 100, 10, 10, 9, None) == 4
     assert f(0x1000, 0x2000, 0x3000, 0, 100, 10, 10, 0, None) == 0   # nothing to do
+
+
+def _dw(lib, x=0x1000, w=0x2000, b=None, y=0x3000, N=1, C_in=4, C_out=4, sp=(8,), k=4, s=2,
+        p=1, op=0, d=1, dt=0, act=0, which=0):
+    nd = len(sp)
+    arr = lambda v: (ctypes.c_int64 * nd)(*C.per_dim(v, nd))  # noqa: E731
+    return lib.ctconv_depthwise_forward_kernel(x, w, b, y, N, C_in, C_out, nd, arr(sp), arr(k),
+                                               arr(s), arr(p), arr(op), arr(d), dt, act, which,
+                                               None)
+
+
+def test_depthwise_validation_before_launch(lib):
+    # Every call below is rejected on the host: none reaches a launch.
+    assert _dw(lib, C_out=6) == 2          # C_out not a multiple of C_in
+    assert _dw(lib, C_in=0) == 2
+    assert _dw(lib, N=-1) == 2
+    assert _dw(lib, x=None) == 1
+    assert _dw(lib, w=None) == 1
+    assert _dw(lib, y=None) == 1
+    assert _dw(lib, x=None, y=None, N=0) == 0  # nothing to do
+    assert _dw(lib, dt=3) == 4
+    assert _dw(lib, act=5) == 3
+    assert _dw(lib, which=3) == 3
+    assert _dw(lib, s=0) == 3
+    assert _dw(lib, op=2) == 3
+    assert _dw(lib, x=0x1004) == 5
+    assert _dw(lib, w=0x2002) == 5
+    assert _dw(lib, b=0x4008) == 5
+    # the row-phase kernel forced on shapes it does not take
+    assert _dw(lib, s=3, k=6, which=1) == 3        # row stride 3
+    assert _dw(lib, d=2, k=3, which=1) == 3        # dilation along the row
+    assert _dw(lib, k=10, s=2, which=1) == 3       # 5 taps per phase
+
+
+@pytest.mark.parametrize("sp,k,s,p,op,d,which", [
+    ((50,), 4, 2, 1, 0, 1, 1),              # k = 2s upsampler
+    ((50,), 8, 4, 2, 0, 1, 1),
+    ((50,), 3, 1, 1, 0, 1, 1),              # stride 1
+    ((50,), 5, 2, 1, 1, 1, 1),              # k mod s != 0, output_padding
+    ((50,), 6, 3, 1, 0, 1, 2),              # stride 3: element kernel
+    ((50,), 3, 2, 1, 1, 2, 2),              # dilation along the row
+    ((50,), 10, 2, 4, 0, 1, 2),             # 5 taps per phase
+    ((20, 22), (4, 4), (2, 2), (1, 1), (0, 0), (1, 1), 1),
+    ((20, 22), (3, 3), (2, 2), (1, 1), (1, 1), (2, 1), 2),  # dilation along H
+    ((20, 22), (8, 4), (4, 2), (2, 1), (0, 0), (1, 1), 1),  # stride 4 along H
+    ((20, 22), (5, 4), (5, 2), (2, 1), (0, 0), (1, 1), 2),  # stride 5 along H
+    ((20, 22), (10, 4), (2, 2), (4, 1), (0, 0), (1, 1), 2), # 5 row taps per phase
+    ((20, 22), (3, 3), (2, 2), (1, 1), (1, 1), (1, 2), 2),
+    ((20, 22), (3, 3), (3, 2), (1, 1), (0, 0), (1, 1), 1),  # any stride along H
+])
+def test_depthwise_kernel_choice(lib, sp, k, s, p, op, d, which):
+    assert C.ctconv_depthwise_query_kernel(2, 8, 16, sp, k, s, p, op, d, 1) == which

@@ -1,0 +1,191 @@
+"""GPU parity of the depthwise transposed convolution (groups = C_in) against
+the CPU oracle's grouped scatter definition, through the C ABI.
+
+Bars: relative L2 <= 1e-5 for fp32 and <= 1e-2 for bf16/fp16 against the
+float64 oracle on the storage-rounded inputs; impulse responses bit-exact;
+the two kernels (row-phase and element) equal in value, since both add the
+taps of an output in the same order.
+"""
+
+import numpy as np
+import pytest
+
+from synth import inputs as I
+
+from gpu_util import TOL, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cc():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    from vision_upsampler_decoders_amd import ctconv
+
+    ctconv.load()
+    return ctconv
+
+
+CASES = [
+    # name, dt, N, C_in, M, spatial, k, s, p, op, d, bias
+    ("k4s2_1d_bf16", "bf16", 2, 6, 1, (300,), (4,), (2,), (1,), (0,), (1,), True),
+    ("k4s2_1d_f32_ragged", "f32", 2, 5, 1, (301,), (4,), (2,), (1,), (1,), (1,), False),
+    ("k8s4_1d_f16_mult2", "f16", 1, 4, 2, (257,), (8,), (4,), (2,), (0,), (1,), True),
+    ("k5s2_1d_bf16_op", "bf16", 2, 3, 1, (131,), (5,), (2,), (2,), (1,), (1,), True),
+    ("k3s1_1d_f32", "f32", 1, 4, 3, (600,), (3,), (1,), (1,), (0,), (1,), True),
+    ("k16s4_1d_bf16", "bf16", 1, 3, 1, (90,), (16,), (4,), (6,), (0,), (1,), False),
+    ("k6s3_1d_f32_element", "f32", 2, 3, 1, (77,), (6,), (3,), (1,), (0,), (1,), True),
+    ("k3s2d2_1d_f16_element", "f16", 2, 3, 2, (64,), (3,), (2,), (1,), (1,), (2,), True),
+    ("k10s2_1d_bf16_element", "bf16", 1, 2, 1, (50,), (10,), (2,), (4,), (0,), (1,), True),
+    ("k4s2_2d_bf16", "bf16", 2, 5, 1, (33, 70), (4, 4), (2, 2), (1, 1), (0, 0), (1, 1), True),
+    ("k3s2op1_2d_f32", "f32", 2, 3, 2, (17, 19), (3, 3), (2, 2), (1, 1), (1, 1), (1, 1), False),
+    ("k3s2_dilH_2d_f16_element", "f16", 1, 4, 1, (12, 40), (3, 3), (2, 2), (1, 1), (1, 1), (2, 1),
+     True),
+    ("k3s2_dil2_2d_f32_element", "f32", 1, 4, 1, (12, 21), (3, 3), (2, 2), (1, 1), (1, 1),
+     (2, 2), True),
+    ("k5x4_s3x4_2d_bf16", "bf16", 1, 3, 2, (9, 130), (5, 4), (3, 4), (2, 1), (1, 0), (1, 1),
+     True),
+    ("k8s4_2d_f32", "f32", 1, 3, 1, (10, 33), (8, 8), (4, 4), (2, 2), (0, 0), (1, 1), True),
+    ("k3s1_2d_bf16", "bf16", 2, 3, 1, (7, 64), (3, 3), (1, 1), (1, 1), (0, 0), (1, 1), False),
+    ("k10s2_2d_f16_element", "f16", 1, 2, 1, (6, 20), (10, 4), (2, 2), (4, 1), (0, 0), (1, 1),
+     True),
+]
+
+
+def _inputs(case):
+    name, dt, N, C_in, M, sp, k, s, p, op, d, has_b = case
+    seed = 900 + 7 * len(name)
+    x64 = I.normal(seed, (N, C_in) + sp, 1.0, dt)
+    w64 = I.normal(seed + 1, (C_in, M) + k, float(np.prod(k)) ** -0.5, dt)
+    b64 = I.uniform(seed + 2, (C_in * M,), -0.1, 0.1, dt) if has_b else None
+    return x64, w64, b64
+
+
+def _dev_run(cc, x64, w64, b64, dt, s, p, op, d, which, act=0):
+    import torch
+
+    y = cc.depthwise_forward(to_dev(x64, dt), to_dev(w64, dt),
+                             None if b64 is None else to_dev(b64, dt), s, p, op, d,
+                             act=act, which=which)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("which", [0, 2], ids=["auto", "element"])
+def test_depthwise_parity(cc, case, which):
+    from oracle import conv_transpose_grouped, rel_l2
+
+    name, dt, N, C_in, M, sp, k, s, p, op, d, has_b = case
+    say(f"depthwise {name} which={which}")
+    x64, w64, b64 = _inputs(case)
+    y = _dev_run(cc, x64, w64, b64, dt, s, p, op, d, which)
+    ref = conv_transpose_grouped(x64, w64, b64, C_in, s, p, op, d)
+    assert tuple(y.shape) == ref.shape
+    err = rel_l2(to_host(y), ref)
+    say(f"  rel_l2 = {err:.3e}")
+    assert err <= TOL[dt], err
+
+
+def test_depthwise_kernel_choice_matches_cases(cc):
+    """The auto cases above cover both kernels: the names say which one runs."""
+    for case in CASES:
+        name, dt, N, C_in, M, sp, k, s, p, op, d, has_b = case
+        which = cc.ctconv_depthwise_query_kernel(N, C_in, C_in * M, sp, k, s, p, op, d)
+        assert which == (2 if name.endswith("_element") else 1), name
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[2], CASES[3], CASES[9], CASES[13]],
+                         ids=lambda c: c[0])
+def test_row_and_element_kernels_agree(cc, case):
+    import torch
+
+    name, dt, N, C_in, M, sp, k, s, p, op, d, has_b = case
+    say(f"row vs element {name}")
+    x64, w64, b64 = _inputs(case)
+    y_row = _dev_run(cc, x64, w64, b64, dt, s, p, op, d, 1)
+    y_el = _dev_run(cc, x64, w64, b64, dt, s, p, op, d, 2)
+    assert torch.equal(y_row, y_el)
+
+
+@pytest.mark.parametrize("case", [CASES[0], CASES[9], CASES[11]], ids=lambda c: c[0])
+def test_depthwise_fused_elu(cc, case):
+    from oracle import conv_transpose_grouped, elu, rel_l2
+
+    name, dt, N, C_in, M, sp, k, s, p, op, d, has_b = case
+    say(f"depthwise elu {name}")
+    x64, w64, b64 = _inputs(case)
+    for which in (0, 2):
+        y = _dev_run(cc, x64, w64, b64, dt, s, p, op, d, which, act=cc.ACT_ELU)
+        ref = elu(conv_transpose_grouped(x64, w64, b64, C_in, s, p, op, d))
+        err = rel_l2(to_host(y), ref)
+        say(f"  which={which} rel_l2 = {err:.3e}")
+        assert err <= TOL[dt], err
+
+
+@pytest.mark.parametrize("which", [1, 2], ids=["row", "element"])
+def test_depthwise_impulse_exact(cc, which):
+    """One input element reaches only its own channel's outputs, with the
+    weights themselves, bit for bit (every dtype)."""
+    import torch
+
+    from oracle import conv_transpose_grouped
+
+    for dt in ("f32", "bf16", "f16"):
+        C, M, H, W, k, s, p = 3, 2, 9, 70, (4, 4), (2, 2), (1, 1)
+        w64 = I.uniform(77, (C, M) + k, -1, 1, dt)
+        for c0, i0, j0 in [(0, 0, 0), (2, H - 1, W - 1), (1, 4, 33)]:
+            x64 = np.zeros((1, C, H, W))
+            x64[0, c0, i0, j0] = 1.0
+            y = _dev_run(cc, x64, w64, None, dt, s, p, 0, 1, which)
+            ref = conv_transpose_grouped(x64, w64, None, C, s, p)
+            assert np.array_equal(to_host(y), ref), (dt, c0, i0, j0)
+    torch.cuda.synchronize()
+
+
+def test_depthwise_empty_input_fills_bias(cc):
+    import torch
+
+    dt = "f32"
+    b64 = I.uniform(5, (6,), -0.1, 0.1, dt)
+    w = to_dev(I.uniform(6, (3, 2, 4), -1, 1, dt), dt)
+    x = torch.empty((2, 3, 0), dtype=torch.float32, device="cuda")
+    # L_in = 0: output length (0 - 1)*2 - 2*0 + 3 + 1 = 2, every element the bias
+    y = cc.depthwise_forward(x, w, to_dev(b64, dt), 2, 0)
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (2, 6, 2)
+    np.testing.assert_array_equal(to_host(y), np.broadcast_to(b64[None, :, None], (2, 6, 2)))
+    x0 = torch.empty((0, 3, 5), dtype=torch.float32, device="cuda")
+    y0 = cc.depthwise_forward(x0, w, None, 2, 1)
+    assert y0.shape[0] == 0
+
+
+@pytest.mark.parametrize("name", ["depthwise2d", "depthwise1d"])
+def test_depthwise_workload_full_size(cc, name):
+    """The benchmark's depthwise workloads at full size, every output."""
+    import torch
+
+    from oracle import conv_transpose_grouped, rel_l2
+
+    wl = I.workload(name)
+    L = wl.layers[0]
+    say(f"full size {name}: generating inputs")
+    x64 = I.gen_x(wl)
+    w64 = I.gen_w(wl)
+    b64 = I.gen_bias(wl)
+    conv = cc.DepthwiseConv(wl.N, L.C_in, L.C_out, wl.in_spatial, L.kernel, L.stride, L.padding,
+                            L.output_padding, L.dilation, {"f32": 0, "bf16": 1, "f16": 2}[wl.dtype])
+    x, w = to_dev(x64, wl.dtype), to_dev(w64, wl.dtype)
+    b = None if b64 is None else to_dev(b64, wl.dtype)
+    y = torch.empty(conv.out_shape(), dtype=x.dtype, device="cuda")
+    say(f"  launch {conv.out_shape()}")
+    conv(x.data_ptr(), w.data_ptr(), None if b is None else b.data_ptr(), y.data_ptr(),
+         int(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    ref = conv_transpose_grouped(x64, w64, b64, L.groups, L.stride, L.padding, L.output_padding,
+                                 L.dilation)
+    err = rel_l2(to_host(y), ref)
+    say(f"  rel_l2 = {err:.3e}")
+    assert err <= TOL[wl.dtype], err

@@ -30,7 +30,7 @@ FLAGS = [
 ]
 
 SOURCES = ["ctconv_api.hip", "prepack.hip", "gather.hip", "pointwise.hip", "stream.hip",
-           "polyphase.hip"]
+           "depthwise.hip", "polyphase.hip"]
 
 
 def _compile(src: str) -> str:

@@ -356,6 +356,99 @@ ctconv_status ctconv_istft_normalize(const void* y, const void* env, void* out, 
                                        static_cast<hipStream_t>(stream)));
 }
 
+// ---------------------------------------------------------------------------
+// Depthwise transposed convolution (groups = C_in)
+// ---------------------------------------------------------------------------
+
+namespace {
+ctconv_status depthwise_problem(int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                                const int64_t* in_spatial, const int64_t* kernel,
+                                const int64_t* stride, const int64_t* padding,
+                                const int64_t* output_padding, const int64_t* dilation,
+                                ctconv_dtype dtype, Problem* p) {
+    memset(p, 0, sizeof(*p));
+    ctconv_status st =
+        geometry(ndim, in_spatial, kernel, stride, padding, output_padding, dilation, p);
+    if (st != CTCONV_OK) return st;
+    if (!dtype_ok(dtype)) return CTCONV_ERR_DTYPE;
+    if (N < 0 || C_in < 1 || C_out < 1 || C_out % C_in != 0) return CTCONV_ERR_SHAPE;
+    p->N = N;
+    p->C_in = C_in;
+    p->C_out = C_out;
+    p->dtype = dtype;
+    int64_t t;
+    // x, w and y byte counts must fit int64
+    if (!mul_ok(N, C_in, &t) || !mul_ok(t, p->H, &t) || !mul_ok(t, p->W, &t) ||
+        !mul_ok(t, (int64_t)esize(dtype), &t))
+        return CTCONV_ERR_SHAPE;
+    if (!mul_ok(C_out, p->kH, &t) || !mul_ok(t, p->kW, &t) ||
+        !mul_ok(t, (int64_t)esize(dtype), &t))
+        return CTCONV_ERR_SHAPE;
+    if (!mul_ok(N, C_out, &t) || !mul_ok(t, p->Ho, &t) || !mul_ok(t, p->Wo, &t) ||
+        !mul_ok(t, (int64_t)esize(dtype), &t))
+        return CTCONV_ERR_SHAPE;
+    if (!depthwise_element_ok(*p)) return CTCONV_ERR_SHAPE;
+    return CTCONV_OK;
+}
+}  // namespace
+
+ctconv_status ctconv_depthwise_query_kernel(int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                                            const int64_t* in_spatial, const int64_t* kernel,
+                                            const int64_t* stride, const int64_t* padding,
+                                            const int64_t* output_padding,
+                                            const int64_t* dilation, ctconv_dtype dtype,
+                                            ctconv_dw_kernel* which) {
+    if (!which) return CTCONV_ERR_NULL;
+    Problem p;
+    const ctconv_status st = depthwise_problem(N, C_in, C_out, ndim, in_spatial, kernel, stride,
+                                               padding, output_padding, dilation, dtype, &p);
+    if (st != CTCONV_OK) return st;
+    *which = depthwise_row_ok(p) ? CTCONV_DW_ROW : CTCONV_DW_ELEMENT;
+    return CTCONV_OK;
+}
+
+ctconv_status ctconv_depthwise_forward_kernel(const void* x, const void* w, const void* bias,
+                                              void* y, int64_t N, int64_t C_in, int64_t C_out,
+                                              int ndim, const int64_t* in_spatial,
+                                              const int64_t* kernel, const int64_t* stride,
+                                              const int64_t* padding,
+                                              const int64_t* output_padding,
+                                              const int64_t* dilation, ctconv_dtype dtype,
+                                              ctconv_activation act, ctconv_dw_kernel which,
+                                              void* stream) {
+    if (which != CTCONV_DW_AUTO && which != CTCONV_DW_ROW && which != CTCONV_DW_ELEMENT)
+        return CTCONV_ERR_PARAM;
+    if (act != CTCONV_ACT_NONE && act != CTCONV_ACT_ELU) return CTCONV_ERR_PARAM;
+    Problem p;
+    const ctconv_status st = depthwise_problem(N, C_in, C_out, ndim, in_spatial, kernel, stride,
+                                               padding, output_padding, dilation, dtype, &p);
+    if (st != CTCONV_OK) return st;
+    p.act = (int)act;
+    const bool x_empty = p.N == 0 || p.H == 0 || p.W == 0;
+    if (!w || (!x && !x_empty) || (!y && p.N != 0)) return CTCONV_ERR_NULL;
+    if ((x && !aligned16(x)) || !aligned16(w) || (y && !aligned16(y)) ||
+        (bias && !aligned16(bias)))
+        return CTCONV_ERR_ALIGN;
+    const bool row_ok = depthwise_row_ok(p);
+    if (which == CTCONV_DW_ROW && !row_ok && !x_empty) return CTCONV_ERR_PARAM;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (p.N == 0) return CTCONV_OK;
+    if (x_empty) return to_status(launch_fill(p, bias, y, s));  // no tap reaches y
+    const bool use_row = which == CTCONV_DW_AUTO ? row_ok : which == CTCONV_DW_ROW;
+    return to_status(launch_depthwise(p, x, w, bias, y, use_row, s));
+}
+
+ctconv_status ctconv_depthwise_forward(const void* x, const void* w, const void* bias, void* y,
+                                       int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                                       const int64_t* in_spatial, const int64_t* kernel,
+                                       const int64_t* stride, const int64_t* padding,
+                                       const int64_t* output_padding, const int64_t* dilation,
+                                       ctconv_dtype dtype, ctconv_activation act, void* stream) {
+    return ctconv_depthwise_forward_kernel(x, w, bias, y, N, C_in, C_out, ndim, in_spatial,
+                                           kernel, stride, padding, output_padding, dilation,
+                                           dtype, act, CTCONV_DW_AUTO, stream);
+}
+
 ctconv_status ctconv_elu(const void* x, void* y, int64_t n, ctconv_dtype dtype, void* stream) {
     if (!x || !y) return CTCONV_ERR_NULL;
     if (!dtype_ok(dtype)) return CTCONV_ERR_DTYPE;

@@ -181,6 +181,15 @@ hipError_t launch_stream_flush(const float* tail_in, const void* bias, void* y, 
                                int64_t C_out, int64_t Tl, ctconv_dtype dt, int act,
                                hipStream_t s);
 
+// Depthwise transposed convolution (groups = C_in, C_out a multiple of C_in;
+// the weight is the unpacked [C_in, C_out / C_in, k...] tensor).
+// depthwise_row_ok: the row-phase kernel covers the shape; depthwise_element_ok:
+// the element kernel's 32-bit fields hold its sizes.
+bool depthwise_row_ok(const Problem& p);
+bool depthwise_element_ok(const Problem& p);
+hipError_t launch_depthwise(const Problem& p, const void* x, const void* w, const void* bias,
+                            void* y, bool row_kernel, hipStream_t s);
+
 // Polyphase planning and launch.  plan_polyphase returns false when no
 // compiled kernel instance covers the shape.
 bool polyphase_supported(const Problem& p);

@@ -23,8 +23,11 @@ EXPORTED = (
     "ctconv_abi_version", "ctconv_status_string", "ctconv_output_shape", "ctconv_packed_bytes",
     "ctconv_prepack", "ctconv_forward", "ctconv_forward_route", "ctconv_forward_act",
     "ctconv_query_route", "ctconv_elu", "ctconv_stream_sizes", "ctconv_stream_step",
-    "ctconv_stream_flush", "ctconv_istft_normalize",
+    "ctconv_stream_flush", "ctconv_istft_normalize", "ctconv_depthwise_forward",
+    "ctconv_depthwise_forward_kernel", "ctconv_depthwise_query_kernel",
 )
+
+DW_AUTO, DW_ROW, DW_ELEMENT = 0, 1, 2
 
 ACT_NONE, ACT_ELU = 0, 1
 
@@ -71,6 +74,13 @@ def load(path: str = LIB_PATH):
     lib.ctconv_query_route.argtypes = [c_i64, c_i64, c_i64, c_int] + [_i64p] * 6 + [
         c_int, ctypes.POINTER(c_int)]
     lib.ctconv_query_route.restype = c_int
+    lib.ctconv_depthwise_forward.argtypes = fwd + [c_int, c_vp]
+    lib.ctconv_depthwise_forward.restype = c_int
+    lib.ctconv_depthwise_forward_kernel.argtypes = fwd + [c_int, c_int, c_vp]
+    lib.ctconv_depthwise_forward_kernel.restype = c_int
+    lib.ctconv_depthwise_query_kernel.argtypes = [c_i64, c_i64, c_i64, c_int] + [_i64p] * 6 + [
+        c_int, ctypes.POINTER(c_int)]
+    lib.ctconv_depthwise_query_kernel.restype = c_int
     lib.ctconv_elu.argtypes = [c_vp, c_vp, c_i64, c_int, c_vp]
     lib.ctconv_elu.restype = c_int
     lib.ctconv_stream_sizes.argtypes = [c_i64, c_i64, c_i64, c_i64, c_i64, c_int, _i64p, _i64p,
@@ -200,6 +210,45 @@ def ctconv_query_route(N: int, C_in: int, C_out: int, in_spatial, kernel, stride
     return r.value
 
 
+def ctconv_depthwise_forward_kernel(x_ptr: int, w_ptr: int, bias_ptr: Optional[int], y_ptr: int,
+                                    N: int, C_in: int, C_out: int, in_spatial, kernel, stride,
+                                    padding, output_padding, dilation, dtype: int, act: int,
+                                    which: int, stream: int) -> None:
+    ndim = len(in_spatial)
+    st = load().ctconv_depthwise_forward_kernel(
+        x_ptr, w_ptr, bias_ptr, y_ptr, N, C_in, C_out, ndim, _arr(in_spatial),
+        _arr(per_dim(kernel, ndim)), _arr(per_dim(stride, ndim)), _arr(per_dim(padding, ndim)),
+        _arr(per_dim(output_padding, ndim)), _arr(per_dim(dilation, ndim)), dtype, act, which,
+        stream)
+    _check("ctconv_depthwise_forward_kernel", st)
+
+
+def ctconv_depthwise_forward(x_ptr: int, w_ptr: int, bias_ptr: Optional[int], y_ptr: int, N: int,
+                             C_in: int, C_out: int, in_spatial, kernel, stride, padding,
+                             output_padding, dilation, dtype: int, act: int,
+                             stream: int) -> None:
+    ndim = len(in_spatial)
+    st = load().ctconv_depthwise_forward(
+        x_ptr, w_ptr, bias_ptr, y_ptr, N, C_in, C_out, ndim, _arr(in_spatial),
+        _arr(per_dim(kernel, ndim)), _arr(per_dim(stride, ndim)), _arr(per_dim(padding, ndim)),
+        _arr(per_dim(output_padding, ndim)), _arr(per_dim(dilation, ndim)), dtype, act, stream)
+    _check("ctconv_depthwise_forward", st)
+
+
+def ctconv_depthwise_query_kernel(N: int, C_in: int, C_out: int, in_spatial, kernel, stride,
+                                  padding=0, output_padding=0, dilation=1,
+                                  dtype: int = CTCONV_F32) -> int:
+    ndim = len(in_spatial)
+    r = ctypes.c_int(-1)
+    st = load().ctconv_depthwise_query_kernel(
+        N, C_in, C_out, ndim, _arr(in_spatial), _arr(per_dim(kernel, ndim)),
+        _arr(per_dim(stride, ndim)), _arr(per_dim(padding, ndim)),
+        _arr(per_dim(output_padding, ndim)), _arr(per_dim(dilation, ndim)), dtype,
+        ctypes.byref(r))
+    _check("ctconv_depthwise_query_kernel", st)
+    return r.value
+
+
 def ctconv_elu(x_ptr: int, y_ptr: int, n: int, dtype: int, stream: int) -> None:
     _check("ctconv_elu", load().ctconv_elu(x_ptr, y_ptr, n, dtype, stream))
 
@@ -299,6 +348,30 @@ def forward(x, packed, bias, C_out: int, kernel, stride, padding=0, output_paddi
     return y
 
 
+def depthwise_forward(x, w, bias, stride, padding=0, output_padding=0, dilation=1,
+                      act: int = ACT_NONE, which: int = DW_AUTO, out=None, stream=None):
+    """y = act(ConvTranspose(x, w, bias, groups=C_in)) for w [C_in, M, k...] (device tensors)."""
+    torch = _torch()
+    if not x.is_cuda or not w.is_cuda:
+        raise ValueError("x and w must be device tensors")
+    x = x.contiguous()
+    w = w.contiguous()
+    ndim = x.dim() - 2
+    N, C_in = x.shape[0], x.shape[1]
+    if w.shape[0] != C_in or w.dim() != ndim + 2:
+        raise ValueError("w must be [C_in, M, k...]")
+    C_out = C_in * w.shape[1]
+    kernel = tuple(w.shape[2:])
+    sp = tuple(x.shape[2:])
+    osp = ctconv_output_shape(sp, kernel, stride, padding, output_padding, dilation)
+    y = out if out is not None else torch.empty((N, C_out) + osp, dtype=x.dtype, device=x.device)
+    bptr = None if bias is None else bias.contiguous().data_ptr()
+    ctconv_depthwise_forward_kernel(x.data_ptr(), w.data_ptr(), bptr, y.data_ptr(), N, C_in,
+                                    C_out, sp, kernel, stride, padding, output_padding, dilation,
+                                    dtype_code(x), act, which, _stream(stream))
+    return y
+
+
 def elu(x, out=None, stream=None):
     torch = _torch()
     x = x.contiguous()
@@ -344,3 +417,20 @@ class Conv:
                       self.ndim, *self._args, self.dtype, self.act, self.route, stream)
         if st != 0:
             raise CtconvError("ctconv_forward_act", st)
+
+
+class DepthwiseConv(Conv):
+    """A depthwise transposed convolution (groups = C_in) with its arguments
+    marshalled once; called with the unpacked weight [C_in, C_out / C_in, k...]."""
+
+    def __init__(self, *args, which: int = DW_AUTO, **kw):
+        kw.pop("route", None)
+        super().__init__(*args, **kw)
+        self.which = which
+        self._fn = load().ctconv_depthwise_forward_kernel
+
+    def __call__(self, x_ptr: int, w_ptr: int, bias_ptr, y_ptr: int, stream: int) -> None:
+        st = self._fn(x_ptr, w_ptr, bias_ptr, y_ptr, self.N, self.C_in, self.C_out,
+                      self.ndim, *self._args, self.dtype, self.act, self.which, stream)
+        if st != 0:
+            raise CtconvError("ctconv_depthwise_forward_kernel", st)
