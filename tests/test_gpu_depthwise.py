@@ -51,6 +51,10 @@ CASES = [
     ("k3s1_2d_bf16", "bf16", 2, 3, 1, (7, 64), (3, 3), (1, 1), (1, 1), (0, 0), (1, 1), False),
     ("k10s2_2d_f16_element", "f16", 1, 2, 1, (6, 20), (10, 4), (2, 2), (4, 1), (0, 0), (1, 1),
      True),
+    # enough work items that a wave walks several (across strips and planes)
+    ("k4s2_2d_bf16_walk", "bf16", 4, 128, 1, (40, 64), (4, 4), (2, 2), (1, 1), (0, 0), (1, 1),
+     True),
+    ("k4s2_1d_f32_walk", "f32", 4, 64, 1, (20000,), (4,), (2,), (1,), (0,), (1,), True),
 ]
 
 

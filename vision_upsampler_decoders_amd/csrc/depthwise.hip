@@ -48,6 +48,8 @@ constexpr int kDwMaxRowStride = 4; // row-phase kernel: stride along H at most 4
 constexpr int kDwMaxRowTaps = 4;   // and ceil(kH / sH) <= 4 input rows per group
 constexpr int kDwBufferWord3 = 0x00020000;  // raw buffer: 32-bit format, range-checked
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 struct DwArgs {
     const void* x;
     const void* w;
@@ -63,6 +65,8 @@ struct DwArgs {
     int segs;            // wave segments (64 * kDwOut outputs) per output row
     int vec;             // 1: Wo % 4 == 0, whole runs of 4 outputs are stored as one vector
     FastDiv fd_segs, fd_NG, fd_Cout, fd_M;
+    int run;             // strip kernel: consecutive work items per wave
+    int segs_base;       // segs for kDwOut outputs per lane (n_items = planes * NG * segs_base)
     int act;
 };
 
@@ -99,10 +103,10 @@ __device__ inline float load_uniform(const void* base, uint32_t e) {
 // the lane's run has tap class j_b = (b + pW) mod SX and reads input column
 // A + g + e_b - r through tap SX*r + j_b, where e_b = 1 when b + (pW mod SX)
 // reaches SX; xv[v] holds input column A - (MX-1) + v.
-template <int SX, int MX>
-__device__ inline void row_taps(float (&acc)[kDwOut], const float (&xv)[kDwOut / SX + MX],
+template <int SX, int MX, int OUT = kDwOut>
+__device__ inline void row_taps(float (&acc)[OUT], const float (&xv)[OUT / SX + MX],
                                 const float (&wv)[SX][MX], int rp) {
-    constexpr int G = kDwOut / SX;
+    constexpr int G = OUT / SX;
 #pragma unroll
     for (int b = 0; b < SX; ++b) {
         // e_b is uniform (rp is a launch constant); both index sets are
@@ -266,6 +270,197 @@ __global__ __launch_bounds__(256) void dw_row_kernel(const DwArgs a) {
     }
 }
 
+// Strip kernel: the row-phase computation with the strides and taps per
+// phase of both dimensions fixed at compile time (SY, MY along H; 1-D has
+// SY = MY = 1).  A wave walks `run` consecutive work items in the order
+// ((plane * segs + seg) * NG + group): down a column strip of one plane in
+// 2-D, along the row in 1-D (there with the grid's stride, see below).  The
+// channel's weights (at most 16) and bias
+// are loaded once per plane into scalar registers; consecutive row groups of
+// a strip share MY - 1 input rows, so each step loads one new row.  All of a
+// step's loads are issued before their first use.
+template <class TR, int SX, int MX, int SY, int MY, int OUT>
+__global__ __launch_bounds__(256) void dw_strip_kernel(const DwArgs a) {
+    using S = typename TR::storage;
+    constexpr int ES = sizeof(S);
+    constexpr int G = OUT / SX;
+    constexpr int NV = G + MX;
+    const int lane = threadIdx.x & 63;
+    const uint32_t wave = uni(blockIdx.x * 4u + threadIdx.x / 64u);
+    uint32_t item = wave * (uint32_t)a.run;
+    if (item >= a.n_items) return;  // uniform
+    const uint32_t item_end =
+        item + (uint32_t)a.run < a.n_items ? item + (uint32_t)a.run : a.n_items;
+
+    const __amdgpu_buffer_rsrc_t xrs =
+        __builtin_amdgcn_make_buffer_rsrc(uni_ptr(a.x), (short)0, (int)a.x_bytes4, kDwBufferWord3);
+    S* __restrict__ yg = static_cast<S*>(a.y);
+    const int q = a.pW / SX, rp = a.pW % SX;
+    const uint32_t row_bytes = (uint32_t)a.W * ES;
+
+    // position of the first item
+    uint32_t g = item % (uint32_t)a.NG;
+    uint32_t t = item / (uint32_t)a.NG;
+    uint32_t seg = t % (uint32_t)a.segs;
+    uint32_t plane = t / (uint32_t)a.segs;
+
+    // per-plane state: weights, bias, x plane offset, y plane
+    float wts[SY][MY][SX][MX];
+    float bv = 0.f;
+    uint32_t xplane = 0;
+    auto load_plane = [&](uint32_t pl) {
+        const uint32_t n = fdiv(pl, a.fd_Cout);
+        const uint32_t co = pl - n * (uint32_t)a.C_out;
+        xplane = uni((n * (uint32_t)a.C_in + fdiv(co, a.fd_M)) * (uint32_t)a.H * row_bytes);
+        const uint32_t wrow = co * (uint32_t)(a.kH * a.kW);
+#pragma unroll
+        for (int jy = 0; jy < SY; ++jy)
+#pragma unroll
+            for (int r = 0; r < MY; ++r) {
+                const int ty = SY * r + jy;
+#pragma unroll
+                for (int b = 0; b < SX; ++b) {
+                    const int jb = b + rp >= SX ? b + rp - SX : b + rp;
+#pragma unroll
+                    for (int rr = 0; rr < MX; ++rr) {
+                        const int tx = SX * rr + jb;
+                        wts[jy][r][b][rr] = (ty < a.kH && tx < a.kW)
+                                                ? load_uniform<TR>(a.w, wrow + ty * a.kW + tx)
+                                                : 0.f;
+                    }
+                }
+            }
+        bv = a.bias != nullptr ? load_uniform<TR>(a.bias, co) : 0.f;
+    };
+    // lane window offsets of segment sg
+    auto lane_offsets = [&](uint32_t sg, uint32_t (&voff)[NV]) {
+        const int A = (((int)sg * 64 + lane) * OUT) / SX + q;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const int col = A - (MX - 1) + v;
+            voff[v] = (uint32_t)col < (uint32_t)a.W ? (uint32_t)col * ES : 0x80000000u;
+        }
+    };
+    // one input row as raw bits (zero outside [0, H)): the loads are issued
+    // unconditionally (a row outside the input gets lane offsets past the
+    // buffer's range) and their values are first used at the next compute,
+    // so that nothing waits for them here
+    auto load_row = [&](int iy, const uint32_t (&voff)[NV], uint32_t (&dst)[NV]) {
+        const bool live = iy >= 0 && iy < a.H;  // uniform
+        const uint32_t rowb = uni(xplane + (uint32_t)(live ? iy : 0) * row_bytes);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            const uint32_t o = live ? voff[v] : 0x80000000u;
+            if constexpr (ES == 2)
+                dst[v] = __builtin_amdgcn_raw_buffer_load_b16(xrs, o, rowb, 0);
+            else
+                dst[v] = __builtin_amdgcn_raw_buffer_load_b32(xrs, o, rowb, 0);
+        }
+    };
+
+    load_plane(plane);
+    uint32_t voff[NV];
+    lane_offsets(seg, voff);
+    uint32_t xv[MY][NV];  // rows ay - r of the current group (raw bits)
+    bool fresh = true;    // the current item starts a strip: all MY rows to load
+
+    for (;;) {
+        // the item's input rows: all of them at the start of a strip, else
+        // the one new row (the others slide down from the previous group);
+        // every load is issued before the first use
+        const int ay = a.ay_min + (int)g;
+        if (fresh) {
+#pragma unroll
+            for (int r = 0; r < MY; ++r) load_row(ay - r, voff, xv[r]);
+        } else {
+#pragma unroll
+            for (int r = MY - 1; r > 0; --r)
+#pragma unroll
+                for (int v = 0; v < NV; ++v) xv[r][v] = xv[r - 1][v];
+            load_row(ay, voff, xv[0]);
+        }
+        float xf[MY][NV];
+#pragma unroll
+        for (int r = 0; r < MY; ++r)
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+                xf[r][v] = ES == 2 ? TR::to_f32((S)xv[r][v]) : __uint_as_float(xv[r][v]);
+
+        // compute and store the group's output rows
+        const int o0 = ((int)seg * 64 + lane) * OUT;
+#pragma unroll
+        for (int jy = 0; jy < SY; ++jy) {
+            const int oy = SY * ay + jy - a.pH;
+            if (oy < 0 || oy >= a.Ho) continue;  // uniform
+            float acc[OUT];
+#pragma unroll
+            for (int u = 0; u < OUT; ++u) acc[u] = 0.f;
+#pragma unroll
+            for (int r = 0; r < MY; ++r) row_taps<SX, MX, OUT>(acc, xf[r], wts[jy][r], rp);
+#pragma unroll
+            for (int u = 0; u < OUT; ++u) acc[u] += bv;
+            if (a.act == CTCONV_ACT_ELU) {  // uniform
+#pragma unroll
+                for (int u = 0; u < OUT; ++u) acc[u] = elu_act<TR>(acc[u]);
+            }
+            S* yr = yg + ((int64_t)plane * a.Ho + oy) * a.Wo;
+            if (a.vec && o0 < a.Wo) {
+                // whole run inside the row, aligned to OUT elements
+                if constexpr (ES == 2) {
+#pragma unroll
+                    for (int c = 0; c < OUT / 8; ++c) {
+                        u32x4 st;
+#pragma unroll
+                        for (int h = 0; h < 4; ++h)
+                            st[h] = (uint32_t)TR::from_f32(acc[8 * c + 2 * h]) |
+                                    ((uint32_t)TR::from_f32(acc[8 * c + 2 * h + 1]) << 16);
+                        *reinterpret_cast<u32x4*>(yr + o0 + 8 * c) = st;
+                    }
+                    if constexpr (OUT % 8 == 4) {
+                        typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+                        u32x2v st;
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+                            st[h] = (uint32_t)TR::from_f32(acc[OUT - 4 + 2 * h]) |
+                                    ((uint32_t)TR::from_f32(acc[OUT - 3 + 2 * h]) << 16);
+                        *reinterpret_cast<u32x2v*>(yr + o0 + OUT - 4) = st;
+                    }
+                } else {
+#pragma unroll
+                    for (int c = 0; c < OUT / 4; ++c) {
+                        f32x4 st;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) st[u] = acc[4 * c + u];
+                        *reinterpret_cast<f32x4*>(yr + o0 + 4 * c) = st;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < OUT; ++u)
+                    if (o0 + u < a.Wo) yr[o0 + u] = TR::from_f32(acc[u]);
+            }
+        }
+
+        // next item: the following row group of the strip, or the start of
+        // the next strip (next segment, or the next plane)
+        if (++item >= item_end) break;  // uniform
+        if (++g < (uint32_t)a.NG) {
+            fresh = false;
+        } else {
+            g = 0;
+            fresh = true;
+            if (++seg == (uint32_t)a.segs) {
+                seg = 0;
+                ++plane;
+                load_plane(plane);
+            }
+            lane_offsets(seg, voff);
+        }
+    }
+}
+
+
+
 template <class TR>
 __global__ __launch_bounds__(256) void dw_element_kernel(const DwArgs a, int64_t total) {
     using S = typename TR::storage;
@@ -353,6 +548,7 @@ bool fill_args(const Problem& p, DwArgs* a) {
     a->x_bytes4 = (uint32_t)((x_bytes + 3) & ~int64_t(3));
     a->n_items = (uint32_t)(p.N * p.C_out * NG * segs);
     a->segs = (int)segs;
+    a->segs_base = (int)segs;
     a->vec = p.Wo % kDwOut == 0;
     a->fd_segs = make_fastdiv((uint32_t)segs);
     a->fd_NG = make_fastdiv((uint32_t)NG);
@@ -370,6 +566,46 @@ hipError_t launch_row(const DwArgs& a, hipStream_t s) {
     const uint32_t waves = a.n_items < waves_max ? a.n_items : waves_max;
     dw_row_kernel<TR, SX, MX><<<dim3((waves + 3) / 4), dim3(256), 0, s>>>(a);
     return hipGetLastError();
+}
+
+// Strip-kernel instances: 1-D (SY = MY = 1, any compiled SX, MX) and 2-D with
+// the same stride and taps per phase in both dimensions and at most 16
+// weights per channel.
+bool strip_shape(int SX, int MX, int SY, int MY) {
+    if (SY == 1 && MY == 1) return true;
+    return SY == SX && MY == MX && SX * MX * SY * MY <= 16;
+}
+
+template <class TR, int SX, int MX, int SY, int MY>
+hipError_t launch_strip(DwArgs a, hipStream_t s) {
+    // 1-D rows are long: 8 outputs per lane; 2-D: 4 (one wave per 256 columns)
+    constexpr int OUT = SY == 1 && MY == 1 ? 8 : 4;
+    const int64_t segs = ((int64_t)a.Wo + 64 * OUT - 1) / (64 * OUT);
+    a.segs = (int)segs;
+    a.fd_segs = make_fastdiv((uint32_t)segs);
+    a.n_items = (uint32_t)((int64_t)a.n_items / a.segs_base * segs);
+    a.vec = a.Wo % OUT == 0;
+    const uint32_t target = (uint32_t)kDwCUs * kDwWavesPerCU;
+    uint32_t run = a.n_items / target;
+    run = run < 1 ? 1 : run > 256 ? 256 : run;
+    a.run = (int)run;
+    const uint32_t waves = (a.n_items + run - 1) / run;
+    dw_strip_kernel<TR, SX, MX, SY, MY, OUT><<<dim3((waves + 3) / 4), dim3(256), 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <class TR>
+hipError_t launch_strip_t(const DwArgs& a, int SX, int MX, int SY, int MY, hipStream_t s) {
+#define CTCONV_DW_STRIP(sx, mx, sy, my) \
+    if (SX == sx && MX == mx && SY == sy && MY == my) return launch_strip<TR, sx, mx, sy, my>(a, s);
+    CTCONV_DW_STRIP(1, 1, 1, 1) CTCONV_DW_STRIP(1, 2, 1, 1) CTCONV_DW_STRIP(1, 3, 1, 1)
+    CTCONV_DW_STRIP(1, 4, 1, 1) CTCONV_DW_STRIP(2, 1, 1, 1) CTCONV_DW_STRIP(2, 2, 1, 1)
+    CTCONV_DW_STRIP(2, 3, 1, 1) CTCONV_DW_STRIP(2, 4, 1, 1) CTCONV_DW_STRIP(4, 1, 1, 1)
+    CTCONV_DW_STRIP(4, 2, 1, 1) CTCONV_DW_STRIP(4, 3, 1, 1) CTCONV_DW_STRIP(4, 4, 1, 1)
+    CTCONV_DW_STRIP(1, 2, 1, 2) CTCONV_DW_STRIP(1, 3, 1, 3) CTCONV_DW_STRIP(1, 4, 1, 4)
+    CTCONV_DW_STRIP(2, 1, 2, 1) CTCONV_DW_STRIP(2, 2, 2, 2) CTCONV_DW_STRIP(4, 1, 4, 1)
+#undef CTCONV_DW_STRIP
+    return hipErrorInvalidValue;
 }
 
 template <class TR>
@@ -441,6 +677,15 @@ hipError_t launch_depthwise(const Problem& p, const void* x, const void* w, cons
         a.w = w;
         a.bias = bias;
         a.y = y;
+        const int SY = (int)p.sH, MY = (int)((p.kH + p.sH - 1) / p.sH);
+        if (strip_shape(SX, MX, SY, MY)) {
+            switch (p.dtype) {
+                case CTCONV_F32: return launch_strip_t<TF32>(a, SX, MX, SY, MY, s);
+                case CTCONV_BF16: return launch_strip_t<TBF16>(a, SX, MX, SY, MY, s);
+                case CTCONV_F16: return launch_strip_t<TF16>(a, SX, MX, SY, MY, s);
+            }
+            return hipErrorInvalidValue;
+        }
         switch (p.dtype) {
             case CTCONV_F32: return launch_row_t<TF32>(a, SX, MX, s);
             case CTCONV_BF16: return launch_row_t<TBF16>(a, SX, MX, s);
