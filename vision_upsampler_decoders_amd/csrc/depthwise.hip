@@ -585,7 +585,9 @@ hipError_t launch_strip(DwArgs a, hipStream_t s) {
     a.fd_segs = make_fastdiv((uint32_t)segs);
     a.n_items = (uint32_t)((int64_t)a.n_items / a.segs_base * segs);
     a.vec = a.Wo % OUT == 0;
-    const uint32_t target = (uint32_t)kDwCUs * kDwWavesPerCU;
+    // resident waves: 32 per CU in 1-D; 24 in 2-D, whose items write two rows
+    // each (measured on the k4 s2 upsamplers: 2-D 111 us at 24, 118 us at 32)
+    const uint32_t target = (uint32_t)kDwCUs * (SY == 1 && MY == 1 ? kDwWavesPerCU : 24);
     uint32_t run = a.n_items / target;
     run = run < 1 ? 1 : run > 256 ? 256 : run;
     a.run = (int)run;
