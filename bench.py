@@ -114,6 +114,17 @@ def load_traffic(workload):
     return None
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(wl, items, frames):
     """The oracle, as it stands, on the first `items` batch items of the
     workload (leading `frames` input positions when frames > 0), every layer
@@ -152,7 +163,7 @@ def cpu_baseline(wl, items, frames):
             "sample": f"batch items 0..{items - 1} of {wl.N}, input {list(sub)} of {list(sp)}, all {len(wl.layers)} "
                       f"layer(s){' with ELU between' if wl.elu_between else ''}; "
                       f"{flops / 1e9:.2f} GFLOP in {dt:.2f} s, single-threaded float64",
-            "seconds": dt, "host_nproc": os.cpu_count()}
+            "seconds": dt, "host_nproc": os.cpu_count(), "host_cpu": cpu_model()}
 
 
 def stream_latency(wl, geo, packed, biases, args, C, dcode, tdt, fuse):
@@ -262,7 +273,7 @@ def main():
 
     log(f"workload {wl.name}: {wl.note}")
     x = dev(I.gen_x(wl))
-    packed, biases, outs, elus = [], [], [], []
+    packed, biases, outs, elus, weights = [], [], [], [], []
     for li, (L, sp, osp, _, _) in enumerate(geo):
         w = dev(I.gen_w(wl, li))
         # a depthwise layer reads its weight as is; a dense one its packed form
@@ -272,7 +283,7 @@ def main():
         outs.append(torch.empty((wl.N, L.C_out) + osp, dtype=tdt, device="cuda"))
         elus.append(torch.empty_like(outs[-1])
                     if (args.separate_elu and wl.elu_between and li + 1 < len(geo)) else None)
-        del w
+        weights.append(w)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     sptr = int(stream.cuda_stream)
@@ -358,6 +369,28 @@ def main():
                              for k in range(args.steps)]))
               for li in range(n_layers) if elus[li] is not None]
 
+    # prepack (once per weight, outside the forward): event-timed per dense layer
+    prepack_us = []
+    for li, (L, sp, osp, _, _) in enumerate(geo):
+        if L.groups > 1:
+            prepack_us.append(None)
+            continue
+        w = weights[li]
+        out_pw = torch.empty_like(packed[li])
+        sz = list(L.kernel)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        C.ctconv_prepack(w.data_ptr(), out_pw.data_ptr(), len(sz), L.C_in, L.C_out, sz, L.stride,
+                         dcode, sptr)
+        e0.record(stream)
+        for _ in range(5):
+            C.ctconv_prepack(w.data_ptr(), out_pw.data_ptr(), len(sz), L.C_in, L.C_out, sz,
+                             L.stride, dcode, sptr)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        assert torch.equal(out_pw, packed[li])
+        prepack_us.append(round(e0.elapsed_time(e1) / 5 * 1e3, 2))
+        del out_pw
+
     total_flops = sum(g[3] for g in geo)
     ms_per_step = wall / args.steps * 1e3
     value = total_flops / (wall / args.steps) / 1e12
@@ -439,6 +472,7 @@ def main():
         "ms_per_step_cold_p10_p50_p90": [round(v / 1e3, 4) for v in pcts(cold_step_ms)],
         "layers": layers,
         "elu_us": [round(v * 1e3, 2) for v in elu_ms],
+        "prepack_us": prepack_us,
         "gflop_per_step": round(total_flops / 1e9, 3),
     }
     if args.stream_frames > 0:
