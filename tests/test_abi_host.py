@@ -294,3 +294,31 @@ def test_depthwise_validation_before_launch(lib):
 ])
 def test_depthwise_kernel_choice(lib, sp, k, s, p, op, d, which):
     assert C.ctconv_depthwise_query_kernel(2, 8, 16, sp, k, s, p, op, d, 1) == which
+
+
+def test_product_path_imports_no_oracle_and_fails_loudly_without_library(tmp_path):
+    """The package and bench's product leg never import the oracle, and the
+    binding raises when libctconv.so is missing (no CPU fallback)."""
+    import ast
+    import importlib
+
+    pkg = os.path.join(ROOT, "vision_upsampler_decoders_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            tree = ast.parse(open(os.path.join(pkg, fn)).read())
+            for node in ast.walk(tree):
+                if isinstance(node, ast.Import):
+                    assert not any(a.name.split(".")[0] == "oracle" for a in node.names), fn
+                if isinstance(node, ast.ImportFrom):
+                    assert (node.module or "").split(".")[0] != "oracle", fn
+    mod = importlib.import_module("vision_upsampler_decoders_amd.ctconv")
+    missing = str(tmp_path / "libctconv_missing.so")
+    saved = mod._lib if hasattr(mod, "_lib") else None
+    try:
+        if hasattr(mod, "_lib"):
+            mod._lib = None
+        with pytest.raises((ImportError, OSError)):
+            mod.load(missing)
+    finally:
+        if hasattr(mod, "_lib"):
+            mod._lib = saved
