@@ -322,3 +322,16 @@ def test_product_path_imports_no_oracle_and_fails_loudly_without_library(tmp_pat
     finally:
         if hasattr(mod, "_lib"):
             mod._lib = saved
+
+
+def test_depthwise_size_limits_choose_element_kernel(lib):
+    """Shapes past the row-phase kernels' 32-bit offsets (x of 2 GiB or more)
+    go to the element kernel; sizes past int64 are rejected (host only, no
+    allocation)."""
+    # bf16 x of 8 * 512 * 2^18 * 2 bytes = 2 GiB: element kernel
+    assert C.ctconv_depthwise_query_kernel(8, 512, 512, (1 << 18,), 4, 2, 1, 0, 1, 1) == 2
+    # just under 2 GiB: row-phase family
+    assert C.ctconv_depthwise_query_kernel(8, 512, 512, ((1 << 18) - 64,), 4, 2, 1, 0, 1, 1) == 1
+    # element counts beyond int64
+    with pytest.raises(C.CtconvError):
+        C.ctconv_depthwise_query_kernel(1 << 40, 1 << 20, 1 << 20, (1 << 20,), 4, 2, 1, 0, 1, 1)
