@@ -43,7 +43,9 @@ namespace {
 
 constexpr int kDwOut = 4;          // outputs per lane along the row
 constexpr int kDwCUs = 256;        // compute units of the chip (grid sizing)
-constexpr int kDwWavesPerCU = 32;  // resident waves per compute unit in the grid
+constexpr int kDwWavesPerCU = 32;  // resident waves per compute unit (row-phase grid)
+constexpr int kDwGridWavesPerCU1D = 512;  // strip kernel, 1-D: grid waves per compute unit
+constexpr int kDwGridWavesPerCU2D = 24;   // strip kernel, 2-D: grid waves per compute unit
 constexpr int kDwMaxRowStride = 4; // row-phase kernel: stride along H at most 4
 constexpr int kDwMaxRowTaps = 4;   // and ceil(kH / sH) <= 4 input rows per group
 constexpr int kDwBufferWord3 = 0x00020000;  // raw buffer: 32-bit format, range-checked
@@ -524,7 +526,7 @@ bool fill_args(const Problem& p, DwArgs* a) {
     // 32-bit lane arithmetic: x below 2^31 bytes (offsets past the range stay
     // below 2^32), work items and all sizes below 2^31, sH * ay below 2^30
     if (x_bytes >= (int64_t(1) << 31) || p.N * p.C_out >= (int64_t(1) << 31) ||
-        p.N * p.C_out * NG * segs >= (int64_t(1) << 31) - kDwCUs * kDwWavesPerCU ||
+        p.N * p.C_out * NG * segs >= (int64_t(1) << 31) - kDwCUs * kDwGridWavesPerCU1D ||
         p.Wo >= (int64_t(1) << 29) || p.Ho + p.pH >= (int64_t(1) << 30) ||
         p.pW >= (int64_t(1) << 30) || p.kH * p.kW >= (1 << 30))
         return false;
@@ -585,9 +587,14 @@ hipError_t launch_strip(DwArgs a, hipStream_t s) {
     a.fd_segs = make_fastdiv((uint32_t)segs);
     a.n_items = (uint32_t)((int64_t)a.n_items / a.segs_base * segs);
     a.vec = a.Wo % OUT == 0;
-    // resident waves: 32 per CU in 1-D; 24 in 2-D, whose items write two rows
-    // each (measured on the k4 s2 upsamplers: 2-D 111 us at 24, 118 us at 32)
-    const uint32_t target = (uint32_t)kDwCUs * (SY == 1 && MY == 1 ? kDwWavesPerCU : 24);
+    // grid size, measured on the k4 s2 upsamplers.  1-D: many short-lived
+    // waves of about two items each, 16x the resident wave slots (as waves
+    // end, new ones start issuing loads at once): 110 us, against 129 us with
+    // a resident grid of 32 per CU walking ~32 items.  2-D: a resident grid
+    // of 24 waves per CU walking down the strips, whose items share input
+    // rows (111 us; 118 at 32; flat from 64 to 256)
+    const uint32_t target =
+        (uint32_t)kDwCUs * (SY == 1 && MY == 1 ? kDwGridWavesPerCU1D : kDwGridWavesPerCU2D);
     uint32_t run = a.n_items / target;
     run = run < 1 ? 1 : run > 256 ? 256 : run;
     a.run = (int)run;
