@@ -88,13 +88,36 @@ def layer_geometry(wl):
     return out
 
 
+def _code_only(text):
+    """Source text without comments and whitespace (a comment edit is no kernel change)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif text[i] in "\"'":
+            q, j = text[i], i + 1
+            while j < n and text[j] != q:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(text[i])
+            i += 1
+    return "".join("".join(out).split())
+
+
 def kernel_source_digest():
+    """sha256 (first 16 hex) of the HIP sources' code, comments and whitespace removed."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "vision_upsampler_decoders_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             h.update(f.encode())
-            h.update(fh.read())
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -16,22 +16,29 @@
 // vector ALUs (a matrix-core formulation would only add traffic).
 //
 // Kernels:
-//  - row-phase kernel (dilation 1; along the row a stride of 1, 2 or 4 and at
-//    most 4 taps per phase; along H a stride of at most 4 and at most 4 taps
-//    per phase): the same phase split is applied along H, where the sH output
-//    rows with one ay = floor((oy + pH) / sH) read the same input rows
-//    ay - r.  One work item is such a row group over 64 * 4 consecutive
-//    columns: a wave loads the group's input rows once (all loads in flight
-//    together), then computes and stores its sH output rows.  The grid is
-//    resident (kDwWavesPerCU waves per compute unit) and each wave walks the
-//    items with the grid's stride, loading the next item's rows before it
-//    computes and stores the current one.  Everything that depends on the rows alone
-//    (input and tap rows, weights, bias) is the same in every lane and lives
-//    in scalar registers; each lane keeps its window of input columns in
-//    registers and its 4 outputs' tap classes are known at compile time up
-//    to one launch constant.
+//  - strip kernel (dilation 1; 1-D shapes with a row stride of 1, 2 or 4 and
+//    at most 4 taps per phase, and 2-D shapes with the same stride and taps
+//    per phase in both dimensions and at most 16 weights per channel): the
+//    phase split is applied along H as well, where the sH output rows with
+//    one ay = floor((oy + pH) / sH) read the same input rows ay - r.  A work
+//    item is such a row group over 64 lanes x 4 outputs (2-D) or a 64 x 8
+//    segment of a row (1-D); a wave walks a run of consecutive items (down
+//    a column strip of one plane in 2-D, sliding one new input row per
+//    step; along the row in 1-D), with the channel's weights and bias loaded
+//    once per plane into scalar registers and every load of a step issued
+//    before its first use.  Strides and taps per phase are compile-time.
+//  - row-phase kernel (the other dilation-1 shapes with at most 4 taps per
+//    phase in each dimension and an H stride of at most 4): the same row
+//    groups over 64 x 4 columns with the row structure at run time; a
+//    resident grid (kDwWavesPerCU waves per compute unit) walks the items
+//    with the grid's stride, issuing the next item's loads before it
+//    computes and stores the current one.
 //  - element kernel (every other shape): one output per lane, taps found from
 //    the tap condition (o + p - t*d divisible by s, quotient inside the input).
+// In the strip and row-phase kernels everything that depends on the rows
+// alone is the same in every lane and lives in scalar registers, each lane
+// keeps its window of input columns in registers, and its outputs' tap
+// classes are known at compile time up to one launch constant.
 
 #include <string.h>
 
@@ -274,10 +281,10 @@ __global__ __launch_bounds__(256) void dw_row_kernel(const DwArgs a) {
 
 // Strip kernel: the row-phase computation with the strides and taps per
 // phase of both dimensions fixed at compile time (SY, MY along H; 1-D has
-// SY = MY = 1).  A wave walks `run` consecutive work items in the order
+// SY = MY = 1) and OUT outputs per lane (8 in 1-D, 4 in 2-D, where rows are
+// shorter).  A wave walks `run` consecutive work items in the order
 // ((plane * segs + seg) * NG + group): down a column strip of one plane in
-// 2-D, along the row in 1-D (there with the grid's stride, see below).  The
-// channel's weights (at most 16) and bias
+// 2-D, along the row in 1-D.  The channel's weights (at most 16) and bias
 // are loaded once per plane into scalar registers; consecutive row groups of
 // a strip share MY - 1 input rows, so each step loads one new row.  All of a
 // step's loads are issued before their first use.
