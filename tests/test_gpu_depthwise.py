@@ -233,3 +233,54 @@ def test_depthwise_graph_replay_and_side_stream(cc):
             _ = (xa.float() * 2).sum().item()  # eager work between replays
             assert torch.equal(ya, ref[j]), (xs, j)
         say(f"depthwise graph {xs} which={which}: 4 replays equal to eager")
+
+
+def _random_cases(n, seed):
+    """Deterministic random depthwise shapes within the kernels' families:
+    1-D and 2-D, strides 1-4 (square and not), taps per phase 1-4, padding,
+    output_padding, multipliers 1-3, widths spanning several 256/512-output
+    segments, and enough items that waves walk across strips and planes."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    cases = []
+    while len(cases) < n:
+        nd = int(rng.integers(1, 3))
+        s = [int(rng.choice([1, 2, 3, 4])) for _ in range(nd)]
+        if nd == 2 and rng.random() < 0.6:
+            s[1] = s[0]
+        k = [int(rng.integers(1, 4 * si + 1)) for si in s]
+        if nd == 2 and s[0] == s[1] and rng.random() < 0.6:
+            k[1] = k[0]
+        p = [int(rng.integers(0, ki)) for ki in k]
+        op = [int(rng.integers(0, si)) for si in s]
+        sp = [int(rng.integers(1, 7))] if nd == 2 else []
+        sp += [int(rng.integers(1, 400))]
+        out = [(a - 1) * b - 2 * c + e + o for a, b, c, e, o in zip(sp, s, p, k, op)]
+        if min(out) < 1:
+            continue
+        N, C, M = int(rng.integers(1, 4)), int(rng.integers(1, 6)), int(rng.integers(1, 4))
+        dt = str(rng.choice(["f32", "bf16", "f16"]))
+        cases.append((dt, N, C, M, tuple(sp), tuple(k), tuple(s), tuple(p), tuple(op)))
+    return cases
+
+
+RANDOM_CASES = _random_cases(48, 2024)
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=[f"r{i}" for i in range(len(RANDOM_CASES))])
+def test_depthwise_random_shapes(cc, case):
+    import torch
+
+    from oracle import conv_transpose_grouped, rel_l2
+
+    dt, N, C, M, sp, k, s, p, op = case
+    x64 = I.normal(1000 + N * C, (N, C) + sp, 1.0, dt)
+    w64 = I.normal(2000 + M, (C, M) + k, float(np.prod(k)) ** -0.5, dt)
+    b64 = I.uniform(3000 + C, (C * M,), -0.1, 0.1, dt)
+    ref = conv_transpose_grouped(x64, w64, b64, C, s, p, op)
+    outs = []
+    for which in (0, 2):
+        y = _dev_run(cc, x64, w64, b64, dt, s, p, op, 1, which)
+        err = rel_l2(to_host(y), ref)
+        assert err <= TOL[dt], (case, which, err)
+        outs.append(y)
+    assert torch.equal(outs[0], outs[1]), case
