@@ -477,3 +477,15 @@ def test_grouped_planted_mistakes_are_caught(oracle_mod, tmp_path, name, monkeyp
             caught = True
             break
     assert caught, f"mutation {name} was not detected"
+
+
+def test_grouped_hand_worked_examples(oracle_mod):
+    with open(os.path.join(HERE, "golden", "hand_worked_grouped.json")) as f:
+        gold = json.load(f)
+    for c in gold["cases"]:
+        x = np.array(c["x"], dtype=np.float64)
+        w = np.array(c["w"], dtype=np.float64)
+        b = None if c["bias"] is None else np.array(c["bias"], dtype=np.float64)
+        y = oracle_mod.conv_transpose_grouped(x, w, b, c["groups"], c["stride"], c["padding"],
+                                              c["output_padding"], c["dilation"])
+        np.testing.assert_array_equal(y, np.array(c["y"], dtype=np.float64), err_msg=c["name"])
