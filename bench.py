@@ -315,10 +315,14 @@ def main():
     n_layers = len(geo)
     # arguments marshalled once per layer: each launch is one foreign call
     fuse = wl.elu_between and not args.separate_elu
-    convs = [(C.DepthwiseConv if L.groups > 1 else C.Conv)(
+    # dense layers go through ctconv_forward_ws: shapes with few output tiles
+    # split their reduction into a workspace (deterministic); the others need none
+    convs = [(C.DepthwiseConv if L.groups > 1 else C.ConvWS)(
                  wl.N, L.C_in, L.C_out, sp, L.kernel, L.stride, L.padding, L.output_padding,
                  L.dilation, dcode, act=C.ACT_ELU if (fuse and li + 1 < len(geo)) else C.ACT_NONE)
              for li, (L, sp, osp, _, _) in enumerate(geo)]
+    wspaces = [torch.empty(max(getattr(cv, "ws_bytes", 0), 16), dtype=torch.uint8, device="cuda")
+               if getattr(cv, "ws_bytes", 0) > 0 else None for cv in convs]
     if any(L.groups not in (1, L.C_in) for L in wl.layers):
         raise SystemExit("grouped layers other than depthwise (groups = C_in) are not built")
     ptrs = []
@@ -336,7 +340,10 @@ def main():
         for li in range(n_layers):
             if ev is not None:
                 ev[li][0].record(stream)
-            convs[li](*ptrs[li], sptr)
+            if wspaces[li] is not None:
+                convs[li](*ptrs[li], sptr, wspaces[li].data_ptr(), wspaces[li].numel())
+            else:
+                convs[li](*ptrs[li], sptr)
             if ev is not None:
                 ev[li][1].record(stream)
             if elus[li] is not None:
@@ -438,6 +445,7 @@ def main():
             "us": round(layer_ms[li] * 1e3, 2),
             "us_p10_p50_p90": pcts(layer_samples[li]),
             "us_cold_p10_p50_p90": pcts(cold_layer_samples[li]),
+            "workspace_bytes": int(wspaces[li].numel()) if wspaces[li] is not None else 0,
             "tflops": round(fl / t / 1e12, 2), "gbps": round(nb / t / 1e9, 1),
             "bound": "mfma" if t_mfma >= t_hbm else "hbm",
             "frac_roofline": round(max(t_mfma, t_hbm) / t, 4),

@@ -72,7 +72,8 @@ typedef enum {
     CTCONV_ERR_PARAM = 3, /* ndim, stride, padding, dilation, output_padding or route invalid */
     CTCONV_ERR_DTYPE = 4, /* unknown dtype */
     CTCONV_ERR_ALIGN = 5, /* a device pointer is not 16-byte aligned */
-    CTCONV_ERR_HIP = 6    /* the HIP runtime reported an error while enqueuing */
+    CTCONV_ERR_HIP = 6,   /* the HIP runtime reported an error while enqueuing */
+    CTCONV_ERR_WORKSPACE = 7 /* workspace NULL or below ctconv_workspace_bytes */
 } ctconv_status;
 
 typedef enum {
@@ -148,6 +149,45 @@ ctconv_status ctconv_forward(const void* x, const void* packed_w, const void* bi
                              const int64_t* stride, const int64_t* padding,
                              const int64_t* output_padding, const int64_t* dilation,
                              ctconv_dtype dtype, void* stream);
+
+/*
+ * Deterministic forward with a caller workspace.
+ *
+ * Shapes with few output tiles (the iSTFT of onnxruntime PR #33978, "[WebGPU]
+ * optimizations for audio models", whose transposed convolution has a single
+ * output channel and a 16392-long reduction) leave most compute units idle
+ * unless the reduction over input channels is split across workgroups.
+ * ctconv_forward never splits it; ctconv_forward_ws may, in fp32: the first
+ * split writes its partial sums to y, each other split to its own slab of
+ * the workspace, and a second kernel adds them to y in a fixed order, then
+ * the bias and the activation.  Every call with the same arguments gives the
+ * same bits (no atomics; the order of the additions is fixed).
+ *
+ * ctconv_workspace_bytes (host only): the bytes ctconv_forward_ws needs for
+ * these arguments (0 when it does not split; then workspace may be NULL).
+ * Validates like ctconv_forward.
+ *
+ * ctconv_forward_ws: ctconv_forward_act with route AUTO and a workspace.
+ *   workspace        device, 16-byte aligned, caller-owned, not retained; its
+ *                    contents on entry are ignored and on return undefined; it
+ *                    must not overlap x, packed_w, bias or y
+ *   workspace_bytes  its size; CTCONV_ERR_WORKSPACE when it is below
+ *                    ctconv_workspace_bytes for these arguments
+ * Two calls must not share a workspace concurrently.  Everything else as in
+ * ctconv_forward_act.
+ */
+ctconv_status ctconv_workspace_bytes(int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                                     const int64_t* in_spatial, const int64_t* kernel,
+                                     const int64_t* stride, const int64_t* padding,
+                                     const int64_t* output_padding, const int64_t* dilation,
+                                     ctconv_dtype dtype, size_t* bytes);
+ctconv_status ctconv_forward_ws(const void* x, const void* packed_w, const void* bias, void* y,
+                                int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                                const int64_t* in_spatial, const int64_t* kernel,
+                                const int64_t* stride, const int64_t* padding,
+                                const int64_t* output_padding, const int64_t* dilation,
+                                ctconv_dtype dtype, ctconv_activation act, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /*
  * ctconv_forward with an explicit route, so the two kernels can be checked

@@ -335,3 +335,40 @@ def test_depthwise_size_limits_choose_element_kernel(lib):
     # element counts beyond int64
     with pytest.raises(C.CtconvError):
         C.ctconv_depthwise_query_kernel(1 << 40, 1 << 20, 1 << 20, (1 << 20,), 4, 2, 1, 0, 1, 1)
+
+
+def test_workspace_bytes(lib):
+    """Only fp32 shapes with too few output tiles split their reduction: the
+    iSTFT (one output channel, 8 x 348 rows) asks for slabs the size of y;
+    16-bit shapes and the large fp32 ones ask for none."""
+    # iSTFT 4098 -> 1, k4096 s1024, 345 frames, N = 8: y has 8 * 356352 floats
+    nb = C.ctconv_workspace_bytes(8, 4098, 1, (345,), 4096, 1024, 0, 0, 1, C.CTCONV_F32)
+    y_bytes = 8 * 356352 * 4
+    assert nb > 0 and nb % y_bytes == 0
+    # one image of it (the per-GPU shard of a batch split): still split
+    assert C.ctconv_workspace_bytes(1, 4098, 1, (345,), 4096, 1024, 0, 0, 1, C.CTCONV_F32) > 0
+    assert C.ctconv_workspace_bytes(8, 512, 256, (2000,), 16, 8, 4, 0, 1, C.CTCONV_BF16) == 0
+    assert C.ctconv_workspace_bytes(4, 128, 64, (96, 96), 3, 2, 1, 1, 2, C.CTCONV_F32) == 0
+    # gather route and empty input: none
+    assert C.ctconv_workspace_bytes(2, 40, 16, (100,), 8, 4, 2, 1, 3, C.CTCONV_F32) == 0
+    assert C.ctconv_workspace_bytes(8, 4098, 1, (0,), 4096, 1024, 0, 0, 1, C.CTCONV_F32) == 0
+    with pytest.raises(C.CtconvError):
+        C.ctconv_workspace_bytes(8, 0, 1, (345,), 4096, 1024, 0, 0, 1, C.CTCONV_F32)
+
+
+def test_forward_ws_validation_before_launch(lib):
+    """A missing or short workspace is rejected on the host (no launch)."""
+    nd = 1
+    arr = lambda v: (ctypes.c_int64 * nd)(*C.per_dim(v, nd))  # noqa: E731
+    need = C.ctconv_workspace_bytes(8, 4098, 1, (345,), 4096, 1024, 0, 0, 1, C.CTCONV_F32)
+
+    def call(ws, nbytes, act=0):
+        return lib.ctconv_forward_ws(0x1000, 0x2000, None, 0x3000, 8, 4098, 1, nd, arr((345,)),
+                                     arr(4096), arr(1024), arr(0), arr(0), arr(1), 0, act, ws,
+                                     nbytes, None)
+
+    assert call(None, 0) == 7
+    assert call(0x4000, need - 16) == 7
+    assert call(0x4008, need) == 5      # misaligned workspace
+    assert call(0x4000, need, act=9) == 3
+    assert "workspace" in C.ctconv_status_string(7)

@@ -1,6 +1,7 @@
 """Build libctconv.so (HIP, gfx950) in-tree with hipcc.
 
-    python -m vision_upsampler_decoders_amd.build
+    python -m vision_upsampler_decoders_amd.build            # every source
+    python -m vision_upsampler_decoders_amd.build --changed  # sources newer than their objects
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 VALU forms
 disabled (-Xclang -target-feature -Xclang -packed-fp32-ops), then linked into
@@ -47,10 +48,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 8) -> str:
+def _stale(src: str) -> bool:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    if not os.path.exists(obj):
+        return True
+    t = os.path.getmtime(obj)
+    deps = [os.path.join(CSRC, src), os.path.join(CSRC, "ctconv_internal.h"),
+            os.path.join(INCLUDE, "ctconv.h")]
+    return any(os.path.getmtime(d) > t for d in deps)
+
+
+def build(jobs: int = 8, changed_only: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    todo = [s for s in SOURCES if _stale(s)] if changed_only else list(SOURCES)
+    if todo:
+        with cf.ThreadPoolExecutor(max_workers=min(jobs, len(todo))) as ex:
+            list(ex.map(_compile, todo))
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -61,4 +75,4 @@ def build(jobs: int = 8) -> str:
 
 
 if __name__ == "__main__":
-    print(build())
+    print(build(changed_only="--changed" in sys.argv[1:]))

@@ -145,6 +145,7 @@ const char* ctconv_status_string(ctconv_status status) {
         case CTCONV_ERR_DTYPE: return "unknown dtype";
         case CTCONV_ERR_ALIGN: return "device pointer not 16-byte aligned";
         case CTCONV_ERR_HIP: return "HIP runtime error";
+        case CTCONV_ERR_WORKSPACE: return "workspace missing or smaller than ctconv_workspace_bytes";
     }
     return "unknown status";
 }
@@ -211,13 +212,17 @@ ctconv_status ctconv_query_route(int64_t N, int64_t C_in, int64_t C_out, int ndi
     return CTCONV_OK;
 }
 
-ctconv_status ctconv_forward_act(const void* x, const void* packed_w, const void* bias, void* y,
-                                 int64_t N, int64_t C_in, int64_t C_out, int ndim,
-                                 const int64_t* in_spatial, const int64_t* kernel,
-                                 const int64_t* stride, const int64_t* padding,
-                                 const int64_t* output_padding, const int64_t* dilation,
-                                 ctconv_dtype dtype, ctconv_activation act, ctconv_route route,
-                                 void* stream) {
+namespace {
+
+// The forward with an optional workspace (ws_bytes bytes at ws): validation,
+// routing and launches.  need_ws receives the workspace the plan asks for.
+ctconv_status forward_impl(const void* x, const void* packed_w, const void* bias, void* y,
+                           int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                           const int64_t* in_spatial, const int64_t* kernel,
+                           const int64_t* stride, const int64_t* padding,
+                           const int64_t* output_padding, const int64_t* dilation,
+                           ctconv_dtype dtype, ctconv_activation act, ctconv_route route,
+                           void* ws, size_t ws_bytes, bool ws_call, void* stream) {
     if (route != CTCONV_ROUTE_AUTO && route != CTCONV_ROUTE_POLYPHASE &&
         route != CTCONV_ROUTE_GATHER)
         return CTCONV_ERR_PARAM;
@@ -231,17 +236,69 @@ ctconv_status ctconv_forward_act(const void* x, const void* packed_w, const void
     const bool x_empty = p.N == 0 || p.H == 0 || p.W == 0;
     if (!packed_w || (!x && !x_empty) || (!y && p.N != 0)) return CTCONV_ERR_NULL;
     if ((x && !aligned16(x)) || !aligned16(packed_w) || (y && !aligned16(y)) ||
-        (bias && !aligned16(bias)))
+        (bias && !aligned16(bias)) || (ws && !aligned16(ws)))
         return CTCONV_ERR_ALIGN;
     if (route == CTCONV_ROUTE_POLYPHASE && !(polyphase_eligible(p) && polyphase_supported(p)) &&
-        !(p.N == 0 || p.H == 0 || p.W == 0))
+        !x_empty)
         return CTCONV_ERR_PARAM;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (p.N == 0) return CTCONV_OK;
-    if (p.H == 0 || p.W == 0) return to_status(launch_fill(p, bias, y, s));  // no tap reaches y
+    if (x_empty) return to_status(launch_fill(p, bias, y, s));  // no tap reaches y
     if (route == CTCONV_ROUTE_AUTO) route = choose_route(p);
-    if (route == CTCONV_ROUTE_POLYPHASE) return to_status(launch_polyphase(p, x, packed_w, bias, y, s));
+    if (route == CTCONV_ROUTE_POLYPHASE) {
+        if (ws_call) {
+            const size_t need = polyphase_workspace_bytes(p);
+            if (need > 0 && (!ws || ws_bytes < need)) return CTCONV_ERR_WORKSPACE;
+        } else {
+            ws = nullptr;
+            ws_bytes = 0;
+        }
+        return to_status(launch_polyphase(p, x, packed_w, bias, y, ws, ws_bytes, s));
+    }
     return to_status(launch_gather(p, x, packed_w, bias, y, s));
+}
+
+}  // namespace
+
+ctconv_status ctconv_forward_act(const void* x, const void* packed_w, const void* bias, void* y,
+                                 int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                                 const int64_t* in_spatial, const int64_t* kernel,
+                                 const int64_t* stride, const int64_t* padding,
+                                 const int64_t* output_padding, const int64_t* dilation,
+                                 ctconv_dtype dtype, ctconv_activation act, ctconv_route route,
+                                 void* stream) {
+    return forward_impl(x, packed_w, bias, y, N, C_in, C_out, ndim, in_spatial, kernel, stride,
+                        padding, output_padding, dilation, dtype, act, route, nullptr, 0, false,
+                        stream);
+}
+
+ctconv_status ctconv_workspace_bytes(int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                                     const int64_t* in_spatial, const int64_t* kernel,
+                                     const int64_t* stride, const int64_t* padding,
+                                     const int64_t* output_padding, const int64_t* dilation,
+                                     ctconv_dtype dtype, size_t* bytes) {
+    if (!bytes) return CTCONV_ERR_NULL;
+    Problem p;
+    const ctconv_status st = build_problem(N, C_in, C_out, ndim, in_spatial, kernel, stride,
+                                           padding, output_padding, dilation, dtype, &p);
+    if (st != CTCONV_OK) return st;
+    const bool x_empty = p.N == 0 || p.H == 0 || p.W == 0;
+    *bytes = (!x_empty && choose_route(p) == CTCONV_ROUTE_POLYPHASE)
+                 ? polyphase_workspace_bytes(p)
+                 : 0;
+    return CTCONV_OK;
+}
+
+ctconv_status ctconv_forward_ws(const void* x, const void* packed_w, const void* bias, void* y,
+                                int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                                const int64_t* in_spatial, const int64_t* kernel,
+                                const int64_t* stride, const int64_t* padding,
+                                const int64_t* output_padding, const int64_t* dilation,
+                                ctconv_dtype dtype, ctconv_activation act, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    return forward_impl(x, packed_w, bias, y, N, C_in, C_out, ndim, in_spatial, kernel, stride,
+                        padding, output_padding, dilation, dtype, act, CTCONV_ROUTE_AUTO,
+                        workspace, workspace_bytes, true, stream);
 }
 
 ctconv_status ctconv_forward_route(const void* x, const void* packed_w, const void* bias, void* y,

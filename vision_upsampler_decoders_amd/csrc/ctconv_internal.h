@@ -145,7 +145,11 @@ struct PolyArgs {
     FastDiv fd_psy, fd_psx;  // strides of the packed weight
     int n_chunks;          // C_in_pad / KC
     int chunks_per_split;  // split over C_in: each blockIdx.y takes this many chunks
-    int atomic_out;        // 1: accumulate with fp32 atomics into a pre-filled y
+    int partial;           // 1: split over C_in; split 0 writes its fp32 partial sums
+                           // (no bias, no activation) to y, split s > 0 to slab s - 1
+                           // of ws, and a second kernel adds them in order
+    float* ws;             // the slabs (partial = 1)
+    int64_t ws_slab;       // elements per slab (the size of y)
     int xcd_remap;         // 1: gridDim.x is a multiple of 8, remap for L2 locality
     uint32_t pw_bytes;     // size of the packed weight (below 2^32)
     int act;               // ctconv_activation of the epilogue
@@ -167,6 +171,9 @@ hipError_t launch_prepack(const Problem& p, const void* w, void* pw, hipStream_t
 hipError_t launch_gather(const Problem& p, const void* x, const void* pw, const void* bias,
                          void* y, hipStream_t s);
 hipError_t launch_fill(const Problem& p, const void* bias, void* y, hipStream_t s);
+// y = act(y + ws[0] + ... + ws[nslab-1] + bias), fp32, added in that order.
+hipError_t launch_split_reduce(const Problem& p, const void* bias, void* y, const void* ws,
+                               int nslab, hipStream_t s);
 hipError_t launch_elu(const void* x, void* y, int64_t n, ctconv_dtype dt, hipStream_t s);
 hipError_t launch_istft_norm(const void* y, const void* env, void* out, int64_t rows,
                              int64_t L_in, int64_t trim, int64_t L_out, ctconv_dtype dt,
@@ -190,10 +197,14 @@ bool depthwise_element_ok(const Problem& p);
 hipError_t launch_depthwise(const Problem& p, const void* x, const void* w, const void* bias,
                             void* y, bool row_kernel, hipStream_t s);
 
-// Polyphase planning and launch.  plan_polyphase returns false when no
-// compiled kernel instance covers the shape.
+// Polyphase planning and launch.  polyphase_supported returns false when no
+// compiled kernel instance covers the shape.  polyphase_workspace_bytes: the
+// workspace the launch splits its reduction into when it may use one (0: no
+// split).  launch_polyphase splits only when ws is given and holds at least
+// that many bytes.
 bool polyphase_supported(const Problem& p);
+size_t polyphase_workspace_bytes(const Problem& p);
 hipError_t launch_polyphase(const Problem& p, const void* x, const void* pw, const void* bias,
-                            void* y, hipStream_t s);
+                            void* y, void* ws, size_t ws_bytes, hipStream_t s);
 
 }  // namespace ctconv

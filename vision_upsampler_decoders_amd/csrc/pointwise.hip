@@ -3,12 +3,16 @@
 // fill: every output element gets bias[co] (or 0).  It serves outputs no tap
 // reaches -- an empty input with a non-empty output, the case onnxruntime PR
 // #33978 ("[WebGPU] optimizations for audio models") fixed by running one
-// pass that writes only the bias or zeros -- and it initialises y before a
-// split-over-C_in launch accumulates into it.
+// pass that writes only the bias or zeros -- and the outputs of a dilated
+// shape that no tap reaches.  It applies the forward call's activation to
+// what it writes.
+//
+// split reduce: the sum of the partial results of a reduction split over
+// input-channel ranges (the first in y, the others in a caller workspace),
+// added in a fixed order, so the result is the same bits on every run; then
+// the bias and the activation.
 //
 // elu: y = x for x > 0, exp(x) - 1 otherwise (alpha = 1), in fp32, one rounding.
-// The fill applies the forward call's activation to what it writes, except
-// before a split-over-C_in accumulation (which never carries an activation).
 
 #include "ctconv_internal.h"
 
@@ -26,6 +30,51 @@ __global__ __launch_bounds__(256) void fill_kernel(const typename TR::storage* _
         typename TR::storage v = TR::from_f32(0.f);
         if (bias) v = bias[(i / plane) % C_out];
         if (act == CTCONV_ACT_ELU) v = TR::from_f32(elu_act<TR>(TR::to_f32(v)));
+        y[i] = v;
+    }
+}
+
+// y[i] = act(((y[i] + ws[0][i]) + ws[1][i]) + ... + bias[co]) in fp32, four
+// elements per thread (total is a multiple of 4, as are the slab offsets).
+__global__ __launch_bounds__(256) void split_reduce_kernel(float4* __restrict__ y,
+                                                           const float4* __restrict__ ws,
+                                                           const float* __restrict__ bias,
+                                                           int64_t nvec, int64_t slab_vec,
+                                                           int nslab, int64_t plane, int64_t C_out,
+                                                           int act) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nvec;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        float4 v = y[i];
+        for (int k = 0; k < nslab; ++k) {
+            const float4 w = ws[k * slab_vec + i];
+            v.x += w.x;
+            v.y += w.y;
+            v.z += w.z;
+            v.w += w.w;
+        }
+        float r[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (bias) r[e] += bias[((4 * i + e) / plane) % C_out];
+            if (act == CTCONV_ACT_ELU) r[e] = elu_act<TF32>(r[e]);
+        }
+        y[i] = make_float4(r[0], r[1], r[2], r[3]);
+    }
+}
+
+// The same for a total that is not a multiple of 4 (one element per thread).
+__global__ __launch_bounds__(256) void split_reduce_kernel_1(float* __restrict__ y,
+                                                             const float* __restrict__ ws,
+                                                             const float* __restrict__ bias,
+                                                             int64_t total, int64_t slab, int nslab,
+                                                             int64_t plane, int64_t C_out,
+                                                             int act) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        float v = y[i];
+        for (int k = 0; k < nslab; ++k) v += ws[k * slab + i];
+        if (bias) v += bias[(i / plane) % C_out];
+        if (act == CTCONV_ACT_ELU) v = elu_act<TF32>(v);
         y[i] = v;
     }
 }
@@ -138,6 +187,23 @@ hipError_t launch_fill(const Problem& p, const void* bias, void* y, hipStream_t 
         case CTCONV_F16: return fill_t<TF16>(p, bias, y, s);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_split_reduce(const Problem& p, const void* bias, void* y, const void* ws,
+                               int nslab, hipStream_t s) {
+    const int64_t plane = p.Ho * p.Wo;
+    const int64_t total = p.N * p.C_out * plane;
+    if (total <= 0) return hipSuccess;
+    if (total % 4 == 0) {
+        split_reduce_kernel<<<dim3((unsigned)grid_for(total / 4)), dim3(256), 0, s>>>(
+            static_cast<float4*>(y), static_cast<const float4*>(ws),
+            static_cast<const float*>(bias), total / 4, total / 4, nslab, plane, p.C_out, p.act);
+    } else {
+        split_reduce_kernel_1<<<dim3((unsigned)grid_for(total)), dim3(256), 0, s>>>(
+            static_cast<float*>(y), static_cast<const float*>(ws),
+            static_cast<const float*>(bias), total, total, nslab, plane, p.C_out, p.act);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_elu(const void* x, void* y, int64_t n, ctconv_dtype dt, hipStream_t s) {

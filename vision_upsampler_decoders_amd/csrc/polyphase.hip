@@ -45,8 +45,10 @@
 // Epilogue: + bias, one rounding to the output type, staged in LDS in output
 // order so that each tile writes contiguous runs of y (the phase interleave
 // and the padding slice cost nothing beyond address arithmetic).  Shapes with
-// few tiles split the C_in reduction across workgroups (fp32 output only) and
-// accumulate with fp32 atomics into a bias-filled y.
+// few tiles may split the C_in reduction across workgroups (fp32 only, when
+// the caller gives a workspace): each split writes its fp32 partial sums to y
+// or to a workspace slab with plain stores, and a second kernel adds them in
+// a fixed order, so results are the same bits on every run.
 
 #include <type_traits>
 
@@ -61,7 +63,6 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_u __attribute__((ext_vector_type(4), aligned(1)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32_a2 __attribute__((aligned(2)));
 
 template <class TR>
 struct Mma;
@@ -257,6 +258,7 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     uint32_t xv1[XODD ? C::XITEMS : 1], xs1[XODD ? C::XITEMS : 1];
     int xsh[C::XITEMS];
     uint32_t xpm[C::XITEMS];
+    int xgv[C::XITEMS];  // first channel of the item's group (odd rows: ragged mask)
     // LDS element offset of the first position row.  Lanes without an item
     // get the 16-byte padding at the end of NP rows (never read by the
     // MFMA operand loads), spread over rows, so that every store is
@@ -277,6 +279,7 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
         }
         xsh[it] = 0;
         xpm[it] = 0;
+        xgv[it] = 0;
         if (qw < xper && q < xitems) {
             const int gx = q % ngx;
             const int r2 = q / ngx;
@@ -310,6 +313,7 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                 xs1[it] = ((xlo[it] + 2u) & 2u) * 8u;
             }
             xlds[it] = (wy * WXP + gx * NP) * RSA + g * VEC;
+            xgv[it] = g * VEC;
             inside = inside && pm == (1u << NP) - 1u && xsh[it] == 0;
         }
     }
@@ -321,9 +325,13 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     // size bounds every access (out-of-range dwords read as zero, no fault).
     const uint32_t ch_bytes = uniform((uint32_t)(HW * C::ES));  // one channel plane
     const bool odd_plane = (ch_bytes & 2u) != 0u;
+    // (the image's extent rounded up to a whole dword: with odd 16-bit rows the
+    // 12-byte load of the last piece of the last channel ends in the dword
+    // that holds the image's last element, and the range check zeroes every
+    // dword that reaches past the size)
     const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
         uniform_ptr(xg + n * a.C_in * HW), (short)0,
-        (int)uniform(ch_bytes * (uint32_t)a.C_in), kBufferWord3);
+        (int)uniform((ch_bytes * (uint32_t)a.C_in + 3u) & ~3u), kBufferWord3);
     const __amdgpu_buffer_rsrc_t brs = __builtin_amdgcn_make_buffer_rsrc(
         uniform_ptr(pwg), (short)0, (int)uniform(a.pw_bytes), kBufferWord3);
 
@@ -402,35 +410,35 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     using BBuf = u32x4[C::BITEMS];
     XBuf xr0, xr1;
     BBuf br0, br1;
+    int cx0 = 0, cx1 = 0;  // chunk held by each register buffer
 
     // Global -> registers.  Loads only: nothing here consumes a loaded value,
-    // so no wait is needed before the MFMAs of the current chunk.  Channels
-    // past C_in (ragged last chunk) load channel 0 of the group and are
-    // zeroed at LDS store time, as are positions outside the row.
-    auto gload = [&](int c, XBuf& xr, BBuf& br) __attribute__((always_inline)) {
+    // so no wait is needed before the MFMAs of the current chunk.
+    auto gload = [&](int c, XBuf& xr, BBuf& br, int& cx) __attribute__((always_inline)) {
+        cx = c;
         const uint32_t cbase = uniform((uint32_t)c * KC);
-        // Channels past C_in (ragged last chunk) start at or past the end of
-        // the image's resource, so the hardware returns zeros for them: the
-        // range check of a raw buffer load covers the scalar offset too and
-        // zeroes each out-of-range dword (checked on gfx950), so every chunk
-        // uses the same load form and no load sits under a branch.
+        // The channel term goes into the per-lane offset, which the raw-buffer
+        // range check covers: channels past C_in (a ragged last chunk) start
+        // at or past the end of the image's resource, so their loads return
+        // zeros and never read outside x.  Every chunk uses the same load form
+        // and no load sits under a branch.
 #pragma unroll
         for (int it = 0; it < C::XITEMS; ++it)
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
+                const uint32_t choff = (cbase + e) * ch_bytes;
                 if constexpr (XODD) {
                     // odd channels sit 2 bytes off the even ones when a plane
-                    // is 2 mod 4 bytes long; their scalar offset drops by 2 so
-                    // that it stays a multiple of 4
+                    // is 2 mod 4 bytes long; their offset drops by 2 so that it
+                    // stays a multiple of 4
                     const bool par = (e & 1) && odd_plane;
                     xr[it][e] = __builtin_bit_cast(
                         u32x3, __builtin_amdgcn_raw_buffer_load_b96(
-                                   xrs, par ? xv1[it] : xv0[it],
-                                   (cbase + e) * ch_bytes - (par ? 2u : 0u), 0));
+                                   xrs, (par ? xv1[it] : xv0[it]) + choff - (par ? 2u : 0u), 0,
+                                   0));
                 } else {
                     xr[it][e] = __builtin_bit_cast(
-                        u32x2, __builtin_amdgcn_raw_buffer_load_b64(xrs, xlo[it],
-                                                                    (cbase + e) * ch_bytes, 0));
+                        u32x2, __builtin_amdgcn_raw_buffer_load_b64(xrs, xlo[it] + choff, 0, 0));
                 }
             }
         // the chunk's channel block (a column tile's rows of one block are
@@ -448,13 +456,19 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     };
     // `inside`: true_type when the caller knows that no item of the wave needs
     // realignment or masks, false_type to decide from wave_inside at run time
-    auto lstore = [&](int st, const XBuf& xr, const BBuf& br, auto inside)
+    auto lstore = [&](int st, const XBuf& xr, const BBuf& br, auto inside, int cx)
                       __attribute__((always_inline)) {
         S* xs = smem + st * C::STAGE;
         S* bs = xs + C::XROWS * RSA;
         const u32x4 z = {0u, 0u, 0u, 0u};
         // the 8-byte pieces of item `it` (odd rows: extracted from the 12
         // loaded bytes at the piece's 2-byte offset)
+        // Odd rows: the resource extends x's extent to a whole dword, so the
+        // first load of the channel after the image's last one may return the
+        // two bytes past it; in a ragged chunk the channels past C_in are
+        // zeroed here (wave-uniform branch, taken in the last chunk only).
+        const int nval = (int)a.C_in - cx * KC;  // valid channels of the chunk
+        const bool ragged = XODD && nval < KC;
         auto pieces = [&](int it, u32x2 (&in)[VEC]) __attribute__((always_inline)) {
 #pragma unroll
             for (int e = 0; e < VEC; ++e) {
@@ -464,6 +478,7 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                     const u32x3 w = xr[it][e];
                     in[e] = u32x2{__builtin_amdgcn_alignbit(w[1], w[0], sh),
                                   __builtin_amdgcn_alignbit(w[2], w[1], sh)};
+                    if (ragged && xgv[it] + e >= nval) in[e] = u32x2{0u, 0u};
                 } else {
                     in[e] = xr[it][e];
                 }
@@ -529,11 +544,11 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     // Bias of each column block's output channel, loaded now so that the
     // epilogue never waits for it.  One unconditional load per block: a
     // column past the phases or past C_out, a split-over-C_in launch (whose
-    // bias is in the pre-filled output) and a missing bias all read past the
+    // bias the reduction adds) and a missing bias all read past the
     // resource's range, which returns zero.
     float bvs[CB];
     {
-        const bool has_bias = a.bias != nullptr && !a.atomic_out;
+        const bool has_bias = a.bias != nullptr && !a.partial;
         const __amdgpu_buffer_rsrc_t bres = __builtin_amdgcn_make_buffer_rsrc(
             uniform_ptr(has_bias ? a.bias : a.pw), (short)0,
             (int)uniform(has_bias ? (uint32_t)(a.C_out * C::ES) : 0u), kBufferWord3);
@@ -665,30 +680,30 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
             // two copies of the loop: with and without edge handling in the
             // LDS stores, so that the chunk step has no branch
             auto run = [&](auto inside) __attribute__((always_inline)) {
-                gload(c_begin, xr0, br0);
-                gload(min(c_begin + 1, c_last), xr1, br1);
-                lstore(0, xr0, br0, inside);
+                gload(c_begin, xr0, br0, cx0);
+                gload(min(c_begin + 1, c_last), xr1, br1, cx1);
+                lstore(0, xr0, br0, inside, cx0);
                 __syncthreads();
                 int i = 0;
                 for (; i + 2 < nck; i += 2) {
                     // chunk i in stage 0, chunk i+1 in buffer 1; buffer 0 is free
                     fused(
-                        0, [&]() __attribute__((always_inline)) { gload(c_begin + i + 2, xr0, br0); },
-                        [&]() __attribute__((always_inline)) { lstore(1, xr1, br1, inside); });
+                        0, [&]() __attribute__((always_inline)) { gload(c_begin + i + 2, xr0, br0, cx0); },
+                        [&]() __attribute__((always_inline)) { lstore(1, xr1, br1, inside, cx1); });
                     __syncthreads();
                     // chunk i+1 in stage 1, chunk i+2 in buffer 0; buffer 1 is free
                     fused(
                         1,
                         [&]() __attribute__((always_inline)) {
-                            gload(min(c_begin + i + 3, c_last), xr1, br1);
+                            gload(min(c_begin + i + 3, c_last), xr1, br1, cx1);
                         },
-                        [&]() __attribute__((always_inline)) { lstore(0, xr0, br0, inside); });
+                        [&]() __attribute__((always_inline)) { lstore(0, xr0, br0, inside, cx0); });
                     __syncthreads();
                 }
                 if (i + 1 < nck) {
                     fused(
                         0, []() {},
-                        [&]() __attribute__((always_inline)) { lstore(1, xr1, br1, inside); });
+                        [&]() __attribute__((always_inline)) { lstore(1, xr1, br1, inside, cx1); });
                     __syncthreads();
                     fused(1, []() {}, []() {});
                 } else {
@@ -700,9 +715,9 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
             else
                 run(std::false_type{});
         } else if constexpr (C::PF == 2) {
-            gload(c_begin, xr0, br0);
-            gload(min(c_begin + 1, c_last), xr1, br1);
-            lstore(0, xr0, br0, std::false_type{});
+            gload(c_begin, xr0, br0, cx0);
+            gload(min(c_begin + 1, c_last), xr1, br1, cx1);
+            lstore(0, xr0, br0, std::false_type{}, cx0);
             __syncthreads();
             // Steady state: chunks i and i+1 with at least one more chunk after
             // them, so every store below is unconditional (a skipped store
@@ -711,44 +726,44 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
             int i = 0;
             for (; i + 2 < nck; i += 2) {
                 // chunk i in stage 0; buffer 0 is free, buffer 1 holds chunk i+1
-                gload(c_begin + i + 2, xr0, br0);
+                gload(c_begin + i + 2, xr0, br0, cx0);
                 compute(0);
-                lstore(1, xr1, br1, std::false_type{});
+                lstore(1, xr1, br1, std::false_type{}, cx1);
                 __syncthreads();
                 // chunk i+1 in stage 1; buffer 1 is free, buffer 0 holds chunk i+2
-                gload(min(c_begin + i + 3, c_last), xr1, br1);
+                gload(min(c_begin + i + 3, c_last), xr1, br1, cx1);
                 compute(1);
-                lstore(0, xr0, br0, std::false_type{});
+                lstore(0, xr0, br0, std::false_type{}, cx0);
                 __syncthreads();
             }
             // last one or two chunks: chunk i in stage 0, chunk i+1 in buffer 1
             compute(0);
             if (i + 1 < nck) {
-                lstore(1, xr1, br1, std::false_type{});
+                lstore(1, xr1, br1, std::false_type{}, cx1);
                 __syncthreads();
                 compute(1);
             }
         } else {
             // one register buffer: chunk c+1 is loaded during the MFMAs of
             // chunk c and stored to the other stage after them
-            gload(c_begin, xr0, br0);
-            lstore(0, xr0, br0, std::false_type{});
+            gload(c_begin, xr0, br0, cx0);
+            lstore(0, xr0, br0, std::false_type{}, cx0);
             __syncthreads();
             int i = 0;
             for (; i + 2 < nck; i += 2) {
-                gload(c_begin + i + 1, xr0, br0);
+                gload(c_begin + i + 1, xr0, br0, cx0);
                 compute(0);
-                lstore(1, xr0, br0, std::false_type{});
+                lstore(1, xr0, br0, std::false_type{}, cx0);
                 __syncthreads();
-                gload(c_begin + i + 2, xr0, br0);
+                gload(c_begin + i + 2, xr0, br0, cx0);
                 compute(1);
-                lstore(0, xr0, br0, std::false_type{});
+                lstore(0, xr0, br0, std::false_type{}, cx0);
                 __syncthreads();
             }
             if (i + 1 < nck) {
-                gload(c_begin + i + 1, xr0, br0);
+                gload(c_begin + i + 1, xr0, br0, cx0);
                 compute(0);
-                lstore(1, xr0, br0, std::false_type{});
+                lstore(1, xr0, br0, std::false_type{}, cx0);
                 __syncthreads();
                 compute(1);
             } else {
@@ -816,9 +831,16 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                         if (pair) {
                             const float f1 = actf(acc[rb][cbp][i] + bv);
                             if constexpr (sizeof(S) == 2) {
-                                // one 4-byte LDS store at 2-byte alignment
-                                // (gfx950 LDS takes unaligned dword accesses)
-                                *reinterpret_cast<u32_a2*>(smem + off) = pack2<TR>(f0, f1);
+                                // one 4-byte LDS store when the pair starts on an
+                                // even element (the parity of off is that of ui:
+                                // wave-uniform), else two 2-byte stores
+                                const uint32_t pk = pack2<TR>(f0, f1);
+                                if ((ui & 1) == 0) {
+                                    *reinterpret_cast<uint32_t*>(smem + off) = pk;
+                                } else {
+                                    smem[off] = (S)(pk & 0xFFFFu);
+                                    smem[off + 1] = (S)(pk >> 16);
+                                }
                             } else {
                                 smem[off] = f0;
                                 smem[off + 1] = f1;
@@ -869,10 +891,13 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
         stage_all(std::false_type{});
     __syncthreads();
 
-    S* __restrict__ yg = static_cast<S*>(a.y);
+    // split s > 0 of a split reduction writes its partial sums to slab s - 1
+    S* __restrict__ yg = (a.partial && blockIdx.y > 0)
+                             ? reinterpret_cast<S*>(a.ws + (int64_t)(blockIdx.y - 1) * a.ws_slab)
+                             : static_cast<S*>(a.y);
     const int nrows = a.TCO * R;
     // (a dilation-reduced problem writes every g-th output: element stores)
-    const bool vec_ok = (SS % VEC) == 0 && !a.atomic_out && (!DIL || (a.gx == 1 && a.gy == 1));
+    const bool vec_ok = (SS % VEC) == 0 && (!DIL || (a.gx == 1 && a.gy == 1));
     if (vec_ok && !a.phase_subset) {
         // Flattened over the tile: chunk e (VEC elements) is row e / cpr,
         // column chunk e % cpr of the staged output, so consecutive lanes
@@ -950,21 +975,11 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
             }
         } else {
             if (!DIL || a.gx == 1) {
-                for (int e = lane; e < lim; e += 64) {
-                    if (a.atomic_out)
-                        atomicAdd(reinterpret_cast<float*>(yg) + gbase + e, TR::to_f32(srow[e]));
-                    else
-                        yg[gbase + e] = srow[e];
-                }
+                for (int e = lane; e < lim; e += 64) yg[gbase + e] = srow[e];
             } else if constexpr (DIL) {
                 // every gx-th output of the real row (dilation-reduced problem)
                 S* yrow = yg + gbase;
-                for (int e = lane; e < lim; e += 64) {
-                    if (a.atomic_out)
-                        atomicAdd(reinterpret_cast<float*>(yrow) + e * a.gx, TR::to_f32(srow[e]));
-                    else
-                        yrow[e * a.gx] = srow[e];
-                }
+                for (int e = lane; e < lim; e += 64) yrow[e * a.gx] = srow[e];
             }
         }
     }
@@ -1075,7 +1090,9 @@ bool get_inst(const Problem& p, int CB, Inst* out) {
 constexpr int64_t kInt32Max = 2147483647;
 
 // Fill PolyArgs for problem p; false when no kernel instance covers it.
-bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
+// allow_split: the reduction may be split over workgroups (a workspace holds
+// the partial sums of all splits but the first).
+bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allow_split) {
     if (p.dH != 1 || p.dW != 1) return false;
     if (p.H == 0 || p.W == 0 || p.N == 0) return false;
     // every staged x load covers 8 bytes of one input row
@@ -1172,8 +1189,8 @@ bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
     a->n_row_tiles = n_row_tiles;
     a->n_chunks = (int)n_chunks;
 
-    // Split the C_in reduction when the tile grid leaves CUs idle (fp32 output
-    // only: partial sums meet through fp32 atomics).  Choose the split that
+    // Split the C_in reduction when the tile grid leaves CUs idle (fp32 only,
+    // with a workspace for the partial sums).  Choose the split that
     // minimises (rounds of workgroups) x (chunks per workgroup).
     const int64_t tiles = n_row_tiles * n_col_tiles;
     int64_t per_cu = (160 * 1024) / in.lds_bytes;
@@ -1181,8 +1198,8 @@ bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
     if (per_cu < 1) per_cu = 1;
     const int64_t slots = 256 * per_cu;
     int best = 1;
-    // (never with a fused activation: partial sums cannot be activated)
-    if (p.dtype == CTCONV_F32 && tiles < 2 * slots && n_chunks >= 8 && p.act == CTCONV_ACT_NONE) {
+    // (the reduction kernel adds the bias and applies the activation)
+    if (allow_split && p.dtype == CTCONV_F32 && tiles < 2 * slots && n_chunks >= 8) {
         double best_cost = 1e300;
         for (int sp = 1; sp <= 64 && sp <= n_chunks; ++sp) {
             const int64_t cps = (n_chunks + sp - 1) / sp;
@@ -1196,7 +1213,9 @@ bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
         }
     }
     a->chunks_per_split = (int)((n_chunks + best - 1) / best);
-    a->atomic_out = best > 1 ? 1 : 0;
+    a->partial = best > 1 ? 1 : 0;
+    a->ws = nullptr;
+    a->ws_slab = p.N * p.C_out * p.Ho * p.Wo;
     a->xcd_remap = (tiles % 8 == 0) ? 1 : 0;
     a->n_tiles = (uint32_t)tiles;
     a->fd_cols = make_fastdiv((uint32_t)n_col_tiles);
@@ -1252,13 +1271,15 @@ bool reduce_dilation(const Problem& p, Problem* q, int* o0y, int* o0x) {
     return true;
 }
 
-// Fill PolyArgs for problem p (any dilation that divides the stride).
-bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits) {
+// Fill PolyArgs for problem p (any dilation that divides the stride).  A
+// dilated problem is never split (its untouched outputs hold the bias).
+bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allow_split) {
     Problem q;
     int o0y = 0, o0x = 0;
     if (!reduce_dilation(p, &q, &o0y, &o0x)) return false;
     if (q.Ho == 0 || q.Wo == 0) return false;
-    if (!plan_core(q, a, inst, splits)) return false;
+    const bool dilated = p.dH > 1 || p.dW > 1;
+    if (!plan_core(q, a, inst, splits, allow_split && !dilated)) return false;
     // dilation is compiled into the 3 x 3-tap 2-D instances only
     if ((p.dH > 1 || p.dW > 1) && !inst->dil) return false;
     // the packed weight is the real one: its size, strides and taps
@@ -1291,28 +1312,46 @@ bool polyphase_supported(const Problem& p) {
     PolyArgs a{};
     Inst in{};
     int sp = 1;
-    return plan(p, &a, &in, &sp);
+    return plan(p, &a, &in, &sp, false);
+}
+
+size_t polyphase_workspace_bytes(const Problem& p) {
+    PolyArgs a{};
+    Inst in{};
+    int sp = 1;
+    if (!plan(p, &a, &in, &sp, true) || sp <= 1) return 0;
+    return (size_t)(sp - 1) * (size_t)a.ws_slab * sizeof(float);
 }
 
 hipError_t launch_polyphase(const Problem& p, const void* x, const void* pw, const void* bias,
-                            void* y, hipStream_t s) {
+                            void* y, void* ws, size_t ws_bytes, hipStream_t s) {
     PolyArgs a{};
     Inst in{};
     int splits = 1;
-    if (!plan(p, &a, &in, &splits)) return hipErrorInvalidValue;
+    if (!plan(p, &a, &in, &splits, ws != nullptr)) return hipErrorInvalidValue;
+    if (splits > 1 && ws_bytes < (size_t)(splits - 1) * (size_t)a.ws_slab * sizeof(float)) {
+        // a workspace too small for this plan: run it unsplit
+        if (!plan(p, &a, &in, &splits, false)) return hipErrorInvalidValue;
+    }
     a.x = x;
     a.pw = pw;
     a.bias = bias;
     a.y = y;
-    // outputs no tap reaches (every one but each d-th under dilation) and
-    // the split-over-C_in accumulation start from the bias
-    if (a.atomic_out || a.gy > 1 || a.gx > 1) {
+    a.ws = static_cast<float*>(ws);
+    const int act = a.act;
+    if (a.partial) a.act = CTCONV_ACT_NONE;  // applied by the reduction
+    // outputs no tap reaches (every one but each d-th under dilation)
+    if (a.gy > 1 || a.gx > 1) {
         const hipError_t e = launch_fill(p, bias, y, s);
         if (e != hipSuccess) return e;
     }
     const int64_t tiles = a.n_tiles;
     hipLaunchKernelGGL(in.fn, dim3((unsigned)tiles, (unsigned)splits), dim3(in.threads), 0, s, a);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.partial) return e;
+    Problem pr = p;
+    pr.act = act;
+    return launch_split_reduce(pr, bias, y, ws, splits - 1, s);
 }
 
 }  // namespace ctconv

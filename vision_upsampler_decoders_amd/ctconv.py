@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libctconv.so")
 CTCONV_F32, CTCONV_BF16, CTCONV_F16 = 0, 1, 2
 ROUTE_AUTO, ROUTE_POLYPHASE, ROUTE_GATHER = 0, 1, 2
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_PARAM", 4: "ERR_DTYPE",
-          5: "ERR_ALIGN", 6: "ERR_HIP"}
+          5: "ERR_ALIGN", 6: "ERR_HIP", 7: "ERR_WORKSPACE"}
 
 EXPORTED = (
     "ctconv_abi_version", "ctconv_status_string", "ctconv_output_shape", "ctconv_packed_bytes",
@@ -25,6 +25,7 @@ EXPORTED = (
     "ctconv_query_route", "ctconv_elu", "ctconv_stream_sizes", "ctconv_stream_step",
     "ctconv_stream_flush", "ctconv_istft_normalize", "ctconv_depthwise_forward",
     "ctconv_depthwise_forward_kernel", "ctconv_depthwise_query_kernel",
+    "ctconv_workspace_bytes", "ctconv_forward_ws",
 )
 
 DW_AUTO, DW_ROW, DW_ELEMENT = 0, 1, 2
@@ -74,6 +75,11 @@ def load(path: str = LIB_PATH):
     lib.ctconv_query_route.argtypes = [c_i64, c_i64, c_i64, c_int] + [_i64p] * 6 + [
         c_int, ctypes.POINTER(c_int)]
     lib.ctconv_query_route.restype = c_int
+    lib.ctconv_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_int] + [_i64p] * 6 + [
+        c_int, ctypes.POINTER(ctypes.c_size_t)]
+    lib.ctconv_workspace_bytes.restype = c_int
+    lib.ctconv_forward_ws.argtypes = fwd + [c_int, c_vp, ctypes.c_size_t, c_vp]
+    lib.ctconv_forward_ws.restype = c_int
     lib.ctconv_depthwise_forward.argtypes = fwd + [c_int, c_vp]
     lib.ctconv_depthwise_forward.restype = c_int
     lib.ctconv_depthwise_forward_kernel.argtypes = fwd + [c_int, c_int, c_vp]
@@ -197,6 +203,32 @@ def ctconv_forward(x_ptr: int, packed_ptr: int, bias_ptr: Optional[int], y_ptr: 
     _check("ctconv_forward", st)
 
 
+def ctconv_workspace_bytes(N: int, C_in: int, C_out: int, in_spatial, kernel, stride, padding=0,
+                           output_padding=0, dilation=1, dtype: int = CTCONV_F32) -> int:
+    ndim = len(in_spatial)
+    nb = ctypes.c_size_t(0)
+    st = load().ctconv_workspace_bytes(
+        N, C_in, C_out, ndim, _arr(in_spatial), _arr(per_dim(kernel, ndim)),
+        _arr(per_dim(stride, ndim)), _arr(per_dim(padding, ndim)),
+        _arr(per_dim(output_padding, ndim)), _arr(per_dim(dilation, ndim)), dtype,
+        ctypes.byref(nb))
+    _check("ctconv_workspace_bytes", st)
+    return int(nb.value)
+
+
+def ctconv_forward_ws(x_ptr: int, packed_ptr: int, bias_ptr: Optional[int], y_ptr: int, N: int,
+                      C_in: int, C_out: int, in_spatial, kernel, stride, padding, output_padding,
+                      dilation, dtype: int, act: int, ws_ptr: Optional[int], ws_bytes: int,
+                      stream: int) -> None:
+    ndim = len(in_spatial)
+    st = load().ctconv_forward_ws(
+        x_ptr, packed_ptr, bias_ptr, y_ptr, N, C_in, C_out, ndim, _arr(in_spatial),
+        _arr(per_dim(kernel, ndim)), _arr(per_dim(stride, ndim)), _arr(per_dim(padding, ndim)),
+        _arr(per_dim(output_padding, ndim)), _arr(per_dim(dilation, ndim)), dtype, act, ws_ptr,
+        ws_bytes, stream)
+    _check("ctconv_forward_ws", st)
+
+
 def ctconv_query_route(N: int, C_in: int, C_out: int, in_spatial, kernel, stride, padding=0,
                        output_padding=0, dilation=1, dtype: int = CTCONV_F32) -> int:
     ndim = len(in_spatial)
@@ -312,6 +344,42 @@ def _stream(stream=None) -> int:
     return int(s.cuda_stream)
 
 
+def _side_stream(stream, device):
+    """The explicit stream when it differs from the current one (else None).
+    Inputs made ready on the current stream (copies by .contiguous(), fresh
+    allocations) must be visible to it, so it first waits for the current
+    stream."""
+    torch = _torch()
+    if stream is None:
+        return None
+    cur = torch.cuda.current_stream(device)
+    if int(stream.cuda_stream) == int(cur.cuda_stream):
+        return None
+    stream.wait_stream(cur)
+    return stream
+
+
+def _claim(side, *tensors):
+    """Tell the caching allocator that these tensors are used on `side`, so
+    their memory is not reused before the work queued there is done."""
+    if side is None:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(side)
+
+
+def _check_tensor(name, t, dtype, device, shape=None, numel=None):
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+
+
 def prepack(w, stride, stream=None):
     """Packed phase-major copy of a ConvTranspose weight w [C_in, C_out, k...] (device)."""
     torch = _torch()
@@ -324,27 +392,79 @@ def prepack(w, stride, stream=None):
     dt = dtype_code(w)
     nb = ctconv_packed_bytes(ndim, C_in, C_out, k, stride, dt)
     packed = torch.empty(nb // w.element_size(), dtype=w.dtype, device=w.device)
+    side = _side_stream(stream, w.device)
     ctconv_prepack(w.data_ptr(), packed.data_ptr(), ndim, C_in, C_out, k, stride, dt,
                    _stream(stream))
+    _claim(side, w, packed)
     return packed
 
 
 def forward(x, packed, bias, C_out: int, kernel, stride, padding=0, output_padding=0,
-            dilation=1, route: int = ROUTE_AUTO, out=None, stream=None, act: int = ACT_NONE):
-    """y = act(ConvTranspose(x, w, bias)) with w given by its packed form (device tensors)."""
+            dilation=1, route: int = ROUTE_AUTO, out=None, stream=None, act: int = ACT_NONE,
+            workspace=None):
+    """y = act(ConvTranspose(x, w, bias)) with w given by its packed form (device tensors).
+
+    packed must be the ctconv_prepack output for this C_in, C_out, kernel,
+    stride and dtype: its byte size is checked against ctconv_packed_bytes.
+    bias (or None) is [C_out] of x's dtype; out (or None) is the contiguous
+    [N, C_out, out_spatial...] tensor of x's dtype to write.  workspace: None
+    (ctconv_forward_act), True (ctconv_forward_ws with a workspace allocated
+    here) or a device tensor of at least ctconv_workspace_bytes bytes
+    (ctconv_forward_ws; route must be ROUTE_AUTO)."""
     torch = _torch()
     if not x.is_cuda:
         raise ValueError("x must be a device tensor")
     x = x.contiguous()
     ndim = x.dim() - 2
+    if ndim not in (1, 2):
+        raise ValueError("x must be [N, C_in, L] or [N, C_in, H, W]")
     N, C_in = x.shape[0], x.shape[1]
     sp = tuple(x.shape[2:])
+    dt = dtype_code(x)
+    kernel = per_dim(kernel, ndim)
+    nb = ctconv_packed_bytes(ndim, C_in, C_out, kernel, stride, dt)
+    _check_tensor("packed", packed, x.dtype, x.device)
+    if not packed.is_contiguous() or packed.numel() * packed.element_size() != nb:
+        raise ValueError(f"packed holds {packed.numel() * packed.element_size()} bytes; "
+                         f"ctconv_packed_bytes gives {nb} for this weight shape, stride and "
+                         f"dtype")
     osp = ctconv_output_shape(sp, kernel, stride, padding, output_padding, dilation)
-    y = out if out is not None else torch.empty((N, C_out) + osp, dtype=x.dtype, device=x.device)
-    bptr = None if bias is None else bias.contiguous().data_ptr()
-    ctconv_forward_act(x.data_ptr(), packed.data_ptr(), bptr, y.data_ptr(), N, C_in, C_out, sp,
-                       kernel, stride, padding, output_padding, dilation, dtype_code(x), act,
-                       route, _stream(stream))
+    if bias is not None:
+        _check_tensor("bias", bias, x.dtype, x.device, numel=C_out)
+        bias = bias.contiguous()
+    if out is not None:
+        _check_tensor("out", out, x.dtype, x.device, shape=(N, C_out) + osp)
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
+        y = out
+    else:
+        y = torch.empty((N, C_out) + osp, dtype=x.dtype, device=x.device)
+    ws = None
+    if workspace is not None:
+        if route != ROUTE_AUTO:
+            raise ValueError("a workspace call takes the automatic route")
+        need = ctconv_workspace_bytes(N, C_in, C_out, sp, kernel, stride, padding,
+                                      output_padding, dilation, dt)
+        if workspace is True:
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+        else:
+            ws = workspace
+            if not ws.is_cuda or ws.device != x.device or not ws.is_contiguous():
+                raise ValueError("workspace must be a contiguous tensor on x's device")
+            if ws.numel() * ws.element_size() < need:
+                raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes; "
+                                 f"ctconv_workspace_bytes gives {need}")
+    side = _side_stream(stream, x.device)
+    bptr = None if bias is None else bias.data_ptr()
+    if ws is None:
+        ctconv_forward_act(x.data_ptr(), packed.data_ptr(), bptr, y.data_ptr(), N, C_in, C_out,
+                           sp, kernel, stride, padding, output_padding, dilation, dt, act,
+                           route, _stream(stream))
+    else:
+        ctconv_forward_ws(x.data_ptr(), packed.data_ptr(), bptr, y.data_ptr(), N, C_in, C_out, sp,
+                          kernel, stride, padding, output_padding, dilation, dt, act,
+                          ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    _claim(side, x, packed, bias, y, ws)
     return y
 
 
@@ -357,26 +477,50 @@ def depthwise_forward(x, w, bias, stride, padding=0, output_padding=0, dilation=
     x = x.contiguous()
     w = w.contiguous()
     ndim = x.dim() - 2
+    if ndim not in (1, 2):
+        raise ValueError("x must be [N, C_in, L] or [N, C_in, H, W]")
     N, C_in = x.shape[0], x.shape[1]
     if w.shape[0] != C_in or w.dim() != ndim + 2:
         raise ValueError("w must be [C_in, M, k...]")
+    _check_tensor("w", w, x.dtype, x.device)
     C_out = C_in * w.shape[1]
     kernel = tuple(w.shape[2:])
     sp = tuple(x.shape[2:])
     osp = ctconv_output_shape(sp, kernel, stride, padding, output_padding, dilation)
-    y = out if out is not None else torch.empty((N, C_out) + osp, dtype=x.dtype, device=x.device)
-    bptr = None if bias is None else bias.contiguous().data_ptr()
+    if bias is not None:
+        _check_tensor("bias", bias, x.dtype, x.device, numel=C_out)
+        bias = bias.contiguous()
+    if out is not None:
+        _check_tensor("out", out, x.dtype, x.device, shape=(N, C_out) + osp)
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
+        y = out
+    else:
+        y = torch.empty((N, C_out) + osp, dtype=x.dtype, device=x.device)
+    side = _side_stream(stream, x.device)
+    bptr = None if bias is None else bias.data_ptr()
     ctconv_depthwise_forward_kernel(x.data_ptr(), w.data_ptr(), bptr, y.data_ptr(), N, C_in,
                                     C_out, sp, kernel, stride, padding, output_padding, dilation,
                                     dtype_code(x), act, which, _stream(stream))
+    _claim(side, x, w, bias, y)
     return y
 
 
 def elu(x, out=None, stream=None):
     torch = _torch()
+    if not x.is_cuda:
+        raise ValueError("x must be a device tensor")
     x = x.contiguous()
-    y = out if out is not None else torch.empty_like(x)
+    if out is not None:
+        _check_tensor("out", out, x.dtype, x.device, shape=tuple(x.shape))
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
+        y = out
+    else:
+        y = torch.empty_like(x)
+    side = _side_stream(stream, x.device)
     ctconv_elu(x.data_ptr(), y.data_ptr(), x.numel(), dtype_code(x), _stream(stream))
+    _claim(side, x, y)
     return y
 
 
@@ -434,3 +578,24 @@ class DepthwiseConv(Conv):
                       self.ndim, *self._args, self.dtype, self.act, self.which, stream)
         if st != 0:
             raise CtconvError("ctconv_depthwise_forward_kernel", st)
+
+
+class ConvWS(Conv):
+    """A transposed convolution through ctconv_forward_ws (deterministic split
+    of the reduction when the shape calls for one), arguments marshalled once;
+    called with the workspace pointer and its size in bytes."""
+
+    def __init__(self, *args, **kw):
+        kw.pop("route", None)
+        super().__init__(*args, **kw)
+        self._fn = load().ctconv_forward_ws
+        self.ws_bytes = ctconv_workspace_bytes(self.N, self.C_in, self.C_out, self.in_spatial,
+                                               self.kernel, self.stride, self.padding,
+                                               self.output_padding, self.dilation, self.dtype)
+
+    def __call__(self, x_ptr: int, packed_ptr: int, bias_ptr, y_ptr: int, stream: int,
+                 ws_ptr=None, ws_bytes: int = 0) -> None:
+        st = self._fn(x_ptr, packed_ptr, bias_ptr, y_ptr, self.N, self.C_in, self.C_out,
+                      self.ndim, *self._args, self.dtype, self.act, ws_ptr, ws_bytes, stream)
+        if st != 0:
+            raise CtconvError("ctconv_forward_ws", st)
