@@ -73,8 +73,13 @@ typedef enum {
     CTCONV_ERR_DTYPE = 4, /* unknown dtype */
     CTCONV_ERR_ALIGN = 5, /* a device pointer is not 16-byte aligned */
     CTCONV_ERR_HIP = 6,   /* the HIP runtime reported an error while enqueuing */
-    CTCONV_ERR_WORKSPACE = 7 /* workspace NULL or below ctconv_workspace_bytes */
+    CTCONV_ERR_WORKSPACE = 7, /* workspace NULL or below ctconv_workspace_bytes */
+    CTCONV_ERR_SCRATCH = 8    /* ctconv_forward_noalloc: the call needs more than
+                                 CTCONV_SCRATCH_BYTES of workspace */
 } ctconv_status;
+
+/* Size of the fixed scratch that ctconv_forward_noalloc uses on each device. */
+#define CTCONV_SCRATCH_BYTES (64u << 20)
 
 typedef enum {
     CTCONV_ROUTE_AUTO = 0,      /* polyphase when eligible, else gather */
@@ -188,6 +193,33 @@ ctconv_status ctconv_forward_ws(const void* x, const void* packed_w, const void*
                                 const int64_t* output_padding, const int64_t* dilation,
                                 ctconv_dtype dtype, ctconv_activation act, void* workspace,
                                 size_t workspace_bytes, void* stream);
+
+/*
+ * ctconv_forward_ws without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is the library's own
+ * fixed scratch: one static device array of CTCONV_SCRATCH_BYTES (64 MiB) per
+ * device, created with the library's code object and held until the process
+ * ends.  The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine); on its first use on a device it looks up the scratch's
+ * address there once.
+ *   Every argument as in ctconv_forward_ws (route AUTO, deterministic).
+ *   CTCONV_ERR_SCRATCH when ctconv_workspace_bytes for these arguments exceeds
+ *   CTCONV_SCRATCH_BYTES (checked on the host before anything is enqueued).
+ * All calls on one device share that device's scratch, and every call that
+ * uses it overwrites it (nothing in it needs to start at zero): calls that
+ * overlap on one device -- on different streams, or from different threads
+ * without ordering -- race and must not be issued.  The stream's device is the
+ * one whose scratch is used.
+ * ctconv_scratch_bytes returns CTCONV_SCRATCH_BYTES.
+ */
+ctconv_status ctconv_forward_noalloc(const void* x, const void* packed_w, const void* bias,
+                                     void* y, int64_t N, int64_t C_in, int64_t C_out, int ndim,
+                                     const int64_t* in_spatial, const int64_t* kernel,
+                                     const int64_t* stride, const int64_t* padding,
+                                     const int64_t* output_padding, const int64_t* dilation,
+                                     ctconv_dtype dtype, ctconv_activation act, void* stream);
+size_t ctconv_scratch_bytes(void);
 
 /*
  * ctconv_forward with an explicit route, so the two kernels can be checked

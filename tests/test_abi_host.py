@@ -372,3 +372,22 @@ def test_forward_ws_validation_before_launch(lib):
     assert call(0x4008, need) == 5      # misaligned workspace
     assert call(0x4000, need, act=9) == 3
     assert "workspace" in C.ctconv_status_string(7)
+
+
+def test_noalloc_rejects_beyond_scratch_before_any_device_call(lib):
+    """ctconv_forward_noalloc checks the workspace it needs against the fixed
+    scratch on the host: a shape needing more is refused (no device call is
+    made, which this GPU-less host would fail)."""
+    assert C.ctconv_scratch_bytes() == 64 << 20
+    need = C.ctconv_workspace_bytes(1, 2048, 2, (1024,), 4096, 2048, 0, 0, 1, C.CTCONV_F32)
+    assert need > C.ctconv_scratch_bytes()
+    nd = 1
+    arr = lambda v: (ctypes.c_int64 * nd)(*C.per_dim(v, nd))  # noqa: E731
+    st = lib.ctconv_forward_noalloc(0x1000, 0x2000, None, 0x3000, 1, 2048, 2, nd, arr((1024,)),
+                                    arr(4096), arr(2048), arr(0), arr(0), arr(1), 0, 0, None)
+    assert st == 8
+    assert "scratch" in C.ctconv_status_string(8)
+    # invalid arguments are still reported as such
+    st = lib.ctconv_forward_noalloc(0x1000, 0x2000, None, 0x3000, 1, 0, 2, nd, arr((1024,)),
+                                    arr(4096), arr(2048), arr(0), arr(0), arr(1), 0, 0, None)
+    assert st == 2

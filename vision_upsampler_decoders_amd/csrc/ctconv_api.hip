@@ -146,6 +146,8 @@ const char* ctconv_status_string(ctconv_status status) {
         case CTCONV_ERR_ALIGN: return "device pointer not 16-byte aligned";
         case CTCONV_ERR_HIP: return "HIP runtime error";
         case CTCONV_ERR_WORKSPACE: return "workspace missing or smaller than ctconv_workspace_bytes";
+        case CTCONV_ERR_SCRATCH:
+            return "the call needs more workspace than the fixed scratch (CTCONV_SCRATCH_BYTES)";
     }
     return "unknown status";
 }

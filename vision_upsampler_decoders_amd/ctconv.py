@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libctconv.so")
 CTCONV_F32, CTCONV_BF16, CTCONV_F16 = 0, 1, 2
 ROUTE_AUTO, ROUTE_POLYPHASE, ROUTE_GATHER = 0, 1, 2
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_PARAM", 4: "ERR_DTYPE",
-          5: "ERR_ALIGN", 6: "ERR_HIP", 7: "ERR_WORKSPACE"}
+          5: "ERR_ALIGN", 6: "ERR_HIP", 7: "ERR_WORKSPACE", 8: "ERR_SCRATCH"}
 
 EXPORTED = (
     "ctconv_abi_version", "ctconv_status_string", "ctconv_output_shape", "ctconv_packed_bytes",
@@ -25,7 +25,8 @@ EXPORTED = (
     "ctconv_query_route", "ctconv_elu", "ctconv_stream_sizes", "ctconv_stream_step",
     "ctconv_stream_flush", "ctconv_istft_normalize", "ctconv_depthwise_forward",
     "ctconv_depthwise_forward_kernel", "ctconv_depthwise_query_kernel",
-    "ctconv_workspace_bytes", "ctconv_forward_ws",
+    "ctconv_workspace_bytes", "ctconv_forward_ws", "ctconv_forward_noalloc",
+    "ctconv_scratch_bytes",
 )
 
 DW_AUTO, DW_ROW, DW_ELEMENT = 0, 1, 2
@@ -80,6 +81,10 @@ def load(path: str = LIB_PATH):
     lib.ctconv_workspace_bytes.restype = c_int
     lib.ctconv_forward_ws.argtypes = fwd + [c_int, c_vp, ctypes.c_size_t, c_vp]
     lib.ctconv_forward_ws.restype = c_int
+    lib.ctconv_forward_noalloc.argtypes = fwd + [c_int, c_vp]
+    lib.ctconv_forward_noalloc.restype = c_int
+    lib.ctconv_scratch_bytes.argtypes = []
+    lib.ctconv_scratch_bytes.restype = ctypes.c_size_t
     lib.ctconv_depthwise_forward.argtypes = fwd + [c_int, c_vp]
     lib.ctconv_depthwise_forward.restype = c_int
     lib.ctconv_depthwise_forward_kernel.argtypes = fwd + [c_int, c_int, c_vp]
@@ -227,6 +232,21 @@ def ctconv_forward_ws(x_ptr: int, packed_ptr: int, bias_ptr: Optional[int], y_pt
         _arr(per_dim(output_padding, ndim)), _arr(per_dim(dilation, ndim)), dtype, act, ws_ptr,
         ws_bytes, stream)
     _check("ctconv_forward_ws", st)
+
+
+def ctconv_forward_noalloc(x_ptr: int, packed_ptr: int, bias_ptr: Optional[int], y_ptr: int,
+                           N: int, C_in: int, C_out: int, in_spatial, kernel, stride, padding,
+                           output_padding, dilation, dtype: int, act: int, stream: int) -> None:
+    ndim = len(in_spatial)
+    st = load().ctconv_forward_noalloc(
+        x_ptr, packed_ptr, bias_ptr, y_ptr, N, C_in, C_out, ndim, _arr(in_spatial),
+        _arr(per_dim(kernel, ndim)), _arr(per_dim(stride, ndim)), _arr(per_dim(padding, ndim)),
+        _arr(per_dim(output_padding, ndim)), _arr(per_dim(dilation, ndim)), dtype, act, stream)
+    _check("ctconv_forward_noalloc", st)
+
+
+def ctconv_scratch_bytes() -> int:
+    return int(load().ctconv_scratch_bytes())
 
 
 def ctconv_query_route(N: int, C_in: int, C_out: int, in_spatial, kernel, stride, padding=0,
