@@ -83,8 +83,13 @@ typedef enum {
 
 typedef enum {
     CTCONV_ROUTE_AUTO = 0,      /* polyphase when eligible, else gather */
-    CTCONV_ROUTE_POLYPHASE = 1, /* force the MFMA polyphase kernel (ERR_PARAM if ineligible) */
-    CTCONV_ROUTE_GATHER = 2     /* force the gather kernel (valid for every shape) */
+    CTCONV_ROUTE_POLYPHASE = 1, /* force the polyphase route, its kernel chosen by shape
+                                   (ERR_PARAM if ineligible) */
+    CTCONV_ROUTE_GATHER = 2,    /* force the gather kernel (valid for every shape) */
+    CTCONV_ROUTE_POLYPHASE_TILED = 3,  /* force the LDS-tiled polyphase MFMA kernel */
+    CTCONV_ROUTE_POLYPHASE_STREAM = 4  /* force the register-weight streaming polyphase
+                                          kernel (16-bit 1-D, stride a multiple of 4,
+                                          ceil(k/s) * C_in rounded up to 32 <= 256) */
 } ctconv_route;
 
 /* Activation applied to every output (after the bias, before the one rounding). */

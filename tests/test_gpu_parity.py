@@ -162,11 +162,17 @@ _ORACLE_CACHE = {}
 
 
 @pytest.mark.parametrize("case", FULL_CASES, ids=[c[0] for c in FULL_CASES])
-@pytest.mark.parametrize("route", [0, 2], ids=["auto", "gather"])
+@pytest.mark.parametrize("route", [0, 2, 3], ids=["auto", "gather", "tiled"])
 def test_full_parity(cc, case, route):
+    """Every route on every case it takes: auto (the streaming polyphase kernel
+    where it applies, else the tiled one, else gather), gather forced, and the
+    tiled polyphase kernel forced."""
     name, dt, N, C_in, C_out, sp, k, s, p, op, d, has_b = case
     if route == 2 and C_in * C_out * int(np.prod(k)) * N * int(np.prod(sp)) > 4e9:
         pytest.skip("gather cross-check limited to small cases")
+    if route == 3 and cc.ctconv_query_route(N, C_in, C_out, sp, k, s, p, op, d,
+                                             cc.dtype_code_of(dt)) != cc.ROUTE_POLYPHASE:
+        pytest.skip("not on the polyphase route")
     say(f"full_parity {name} route={route} dt={dt} N={N} C_in={C_in} C_out={C_out} sp={sp}")
     seed = 500 + len(name)
     x64 = I.normal(seed, (N, C_in) + sp, 1.0, dt)

@@ -31,7 +31,7 @@ FLAGS = [
 ]
 
 SOURCES = ["ctconv_api.hip", "prepack.hip", "gather.hip", "pointwise.hip", "stream.hip",
-           "depthwise.hip", "polyphase.hip", "noalloc.hip"]
+           "depthwise.hip", "polyphase.hip", "polyrw.hip", "noalloc.hip"]
 
 
 def _compile(src: str) -> str:
@@ -54,7 +54,7 @@ def _stale(src: str) -> bool:
         return True
     t = os.path.getmtime(obj)
     deps = [os.path.join(CSRC, src), os.path.join(CSRC, "ctconv_internal.h"),
-            os.path.join(INCLUDE, "ctconv.h")]
+            os.path.join(CSRC, "mfma_common.h"), os.path.join(INCLUDE, "ctconv.h")]
     return any(os.path.getmtime(d) > t for d in deps)
 
 

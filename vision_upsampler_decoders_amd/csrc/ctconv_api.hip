@@ -130,6 +130,13 @@ ctconv_route choose_route(const Problem& p) {
     return CTCONV_ROUTE_GATHER;
 }
 
+// The polyphase kernel for a shape on the polyphase route: the streaming
+// kernel when it applies (weights in registers: short reductions), else the
+// tiled one.
+ctconv_route polyphase_kernel(const Problem& p) {
+    return polyrw_supported(p) ? CTCONV_ROUTE_POLYPHASE_STREAM : CTCONV_ROUTE_POLYPHASE_TILED;
+}
+
 }  // namespace
 
 extern "C" {
@@ -226,7 +233,8 @@ ctconv_status forward_impl(const void* x, const void* packed_w, const void* bias
                            ctconv_dtype dtype, ctconv_activation act, ctconv_route route,
                            void* ws, size_t ws_bytes, bool ws_call, void* stream) {
     if (route != CTCONV_ROUTE_AUTO && route != CTCONV_ROUTE_POLYPHASE &&
-        route != CTCONV_ROUTE_GATHER)
+        route != CTCONV_ROUTE_GATHER && route != CTCONV_ROUTE_POLYPHASE_TILED &&
+        route != CTCONV_ROUTE_POLYPHASE_STREAM)
         return CTCONV_ERR_PARAM;
     if (act != CTCONV_ACT_NONE && act != CTCONV_ACT_ELU) return CTCONV_ERR_PARAM;
     Problem p;
@@ -240,14 +248,20 @@ ctconv_status forward_impl(const void* x, const void* packed_w, const void* bias
     if ((x && !aligned16(x)) || !aligned16(packed_w) || (y && !aligned16(y)) ||
         (bias && !aligned16(bias)) || (ws && !aligned16(ws)))
         return CTCONV_ERR_ALIGN;
-    if (route == CTCONV_ROUTE_POLYPHASE && !(polyphase_eligible(p) && polyphase_supported(p)) &&
+    const bool poly_ok = polyphase_eligible(p) && polyphase_supported(p);
+    if ((route == CTCONV_ROUTE_POLYPHASE || route == CTCONV_ROUTE_POLYPHASE_TILED) && !poly_ok &&
         !x_empty)
+        return CTCONV_ERR_PARAM;
+    if (route == CTCONV_ROUTE_POLYPHASE_STREAM && !polyrw_supported(p) && !x_empty)
         return CTCONV_ERR_PARAM;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (p.N == 0) return CTCONV_OK;
     if (x_empty) return to_status(launch_fill(p, bias, y, s));  // no tap reaches y
     if (route == CTCONV_ROUTE_AUTO) route = choose_route(p);
-    if (route == CTCONV_ROUTE_POLYPHASE) {
+    if (route == CTCONV_ROUTE_POLYPHASE) route = polyphase_kernel(p);
+    if (route == CTCONV_ROUTE_POLYPHASE_STREAM)
+        return to_status(launch_polyrw(p, x, packed_w, bias, y, s));
+    if (route == CTCONV_ROUTE_POLYPHASE_TILED) {
         if (ws_call) {
             const size_t need = polyphase_workspace_bytes(p);
             if (need > 0 && (!ws || ws_bytes < need)) return CTCONV_ERR_WORKSPACE;

@@ -204,6 +204,11 @@ hipError_t launch_depthwise(const Problem& p, const void* x, const void* w, cons
 // that many bytes.
 bool polyphase_supported(const Problem& p);
 size_t polyphase_workspace_bytes(const Problem& p);
+// The register-weight streaming kernel (16-bit 1-D, stride a multiple of 4,
+// taps x padded input channels <= 256): never splits, needs no workspace.
+bool polyrw_supported(const Problem& p);
+hipError_t launch_polyrw(const Problem& p, const void* x, const void* pw, const void* bias,
+                         void* y, hipStream_t s);
 hipError_t launch_polyphase(const Problem& p, const void* x, const void* pw, const void* bias,
                             void* y, void* ws, size_t ws_bytes, hipStream_t s);
 

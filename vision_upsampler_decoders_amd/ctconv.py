@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libctconv.so")
 
 CTCONV_F32, CTCONV_BF16, CTCONV_F16 = 0, 1, 2
 ROUTE_AUTO, ROUTE_POLYPHASE, ROUTE_GATHER = 0, 1, 2
+# the two polyphase kernels, forced (cross-checks)
+ROUTE_POLYPHASE_TILED, ROUTE_POLYPHASE_STREAM = 3, 4
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_PARAM", 4: "ERR_DTYPE",
           5: "ERR_ALIGN", 6: "ERR_HIP", 7: "ERR_WORKSPACE", 8: "ERR_SCRATCH"}
 
@@ -356,6 +358,11 @@ def dtype_code(t) -> int:
     if t.dtype not in m:
         raise TypeError(f"unsupported dtype {t.dtype}")
     return m[t.dtype]
+
+
+def dtype_code_of(name: str) -> int:
+    """"f32" / "bf16" / "f16" -> the ctconv_dtype code."""
+    return {"f32": CTCONV_F32, "bf16": CTCONV_BF16, "f16": CTCONV_F16}[name]
 
 
 def _stream(stream=None) -> int:
