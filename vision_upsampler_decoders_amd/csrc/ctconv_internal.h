@@ -122,12 +122,10 @@ struct PolyArgs {
     const void* bias;
     void* y;
     int64_t N, C_in, C_out, C_in_pad;
-    int64_t H, W, Ho, Wo;
-    int sy, sx, py, px;
+    int64_t H, W, Ho, Wo;  // Ho, Wo: outputs of the padding-free problem run
+    int sy, sx;
     int P, T;
     int Ay, Ax;            // output rows per dimension in units of the stride
-    int dminy, dminx;      // floor(p / s)
-    int spready, spreadx;  // 1 when floor((b + p) / s) differs between phases
     int WY, WX;            // x window per tile (rows x columns)
     int xofs;              // window start moved back by this many positions so
                            // that every x load is 8-byte aligned (0 when rows
@@ -159,6 +157,11 @@ struct PolyArgs {
     // Identity (g = 1, o0 = 0, real sizes = Ho, Wo) without dilation.
     int gy, gx, o0y, o0x;
     int64_t HoR, WoR;      // real output sizes (addressing of y)
+    // Padding as an output shift: the kernel computes the transposed
+    // convolution without padding (of the dilation-reduced problem under
+    // dilation) and writes its output o' as output o' - os of that problem
+    // when it lies inside, i.e. below Ho - os (Wo - os)
+    int oys, oxs;
     // Packed-weight geometry (the real stride and taps the weight was packed
     // with): effective tap (s_e*r + j) per dimension is real tap t, stored as
     // phase t mod ps, tap t / ps; taps t >= k read as zero.

@@ -73,11 +73,11 @@ struct Cfg {
     static constexpr int BN = WN * CB * 16;
     static constexpr int TAY = BM / TAX;
     static constexpr int T = MY * MX;
-    static constexpr int WYM = TAY + MY - 1 + (TAY > 1 ? 1 : 0);  // window rows (max)
+    static constexpr int WYM = TAY + MY - 1;  // window rows
     static constexpr int NP = 8 / ES;                             // positions per load item
-    // window columns: the tile, the halo, the shift class and up to NP-1
-    // positions of alignment shift, padded to whole fragments
-    static constexpr int WXP = (TAX + MX + NP - 1 + VEC - 1) / VEC * VEC;
+    // window columns: the tile, the halo and up to NP-1 positions of
+    // alignment shift, padded to whole fragments
+    static constexpr int WXP = (TAX + MX - 1 + NP - 1 + VEC - 1) / VEC * VEC;
     static constexpr int XROWS = WYM * WXP;
     static constexpr int BROWS = T * BN;
     static constexpr int STAGE = (XROWS + BROWS) * RSA;
@@ -138,8 +138,10 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     const int co0 = cq * a.TCO;
     const int b0 = (col_tile - cq * a.n_ph_tiles) * a.PT;
     const int ay0 = ty_t * C::TAY, ax0 = tx_t * TAX;
-    const int wy0 = ay0 + a.dminy - (MY - 1);
-    const int wx0 = ax0 + a.dminx - (MX - 1) - a.xofs;
+    // output phase row q takes input rows q - r, r < m: the window starts
+    // m - 1 rows before the tile
+    const int wy0 = ay0 - (MY - 1);
+    const int wx0 = ax0 - (MX - 1) - a.xofs;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
@@ -261,8 +263,8 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
             const int co = co0 + tc - pb * a.TCO, b = b0 + pb;
             if (pb < a.PT && b < a.P && co < a.C_out) {
                 const int by = (int)fdiv((uint32_t)b, a.fd_sx), bx = b - by * a.sx;
-                const int jy = by + a.py - (int)fdiv((uint32_t)(by + a.py), a.fd_sy) * a.sy;
-                const int jx = bx + a.px - (int)fdiv((uint32_t)(bx + a.px), a.fd_sx) * a.sx;
+                // without padding, output phase b is weight phase b
+                const int jy = by, jx = bx;
                 if (!DIL || (a.gy == 1 && a.gx == 1)) {
                     // packed layout [j][ci / 32][co][r][ci % 32]: row (co, r)
                     // of phase j in channel block 0 (the chunk adds its block)
@@ -291,22 +293,6 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
             }
             blds[it] = (r * BN + tc) * RSA + piece * VEC;
         }
-    }
-
-    // ---- per-wave column-block phase shifts (wave-uniform, kept in SGPRs) --
-    int ddy[CB], ddx[CB];
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-        const int tc0 = (wn * CB + cb) * 16;
-        const int pb = (int)fdiv((uint32_t)tc0, a.fd_tco), b = b0 + pb;
-        int dy = 0, dx = 0;
-        if (pb < a.PT && b < a.P) {
-            const int by = (int)fdiv((uint32_t)b, a.fd_sx), bx = b - by * a.sx;
-            dy = (int)fdiv((uint32_t)(by + a.py), a.fd_sy) - a.dminy;
-            dx = (int)fdiv((uint32_t)(bx + a.px), a.fd_sx) - a.dminx;
-        }
-        ddy[cb] = __builtin_amdgcn_readfirstlane(dy);
-        ddx[cb] = __builtin_amdgcn_readfirstlane(dx);
     }
 
     // Two register buffers: the loads of chunk c+2 are issued before the
@@ -471,73 +457,46 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
         }
     }
 
-    // Shift bookkeeping: column block cb belongs to class (dd_y, dd_x) with
-    // dd in {0, 1} per dimension; for tap (ry, rx) its A rows sit at window
-    // offset (dd_y + MY-1-ry, dd_x + MX-1-rx).  Classes and their presence
-    // mask are wave-uniform.  Per k-step: B fragments of every tap (loaded
-    // once when they fit in registers), then for each class present the A
-    // fragments of all taps, then that class's MFMAs.
-    constexpr bool Y2 = C::TAY > 1;  // 2-D tile: the row offset may differ too
-    int cls[CB];
-    uint32_t clsmask = 0;
+    // Per chunk and k-step, tap by tap: the tap's B fragments, its A
+    // fragments (window rows shifted back by the tap index: output phase row
+    // q takes input q - r) and the MFMAs of every (row block, column block)
+    // pair.  A scheduling barrier between taps keeps one tap's fragments live
+    // at a time.
+    auto tap_step = [&](const S* xs, const S* bs, int kofs, int r) __attribute__((always_inline)) {
+        const int ry = r / MX, rx = r % MX;
+        u32x4 afr[RB], bfr[CB];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-        cls[cb] = (Y2 ? ddy[cb] * 2 : 0) + ddx[cb];
-        clsmask |= 1u << cls[cb];
-    }
+        for (int cb = 0; cb < CB; ++cb)
+            bfr[cb] = *reinterpret_cast<const u32x4*>(bs + (r * BN + bcol + cb * 16) * RSA + kofs);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+            afr[rb] = *reinterpret_cast<const u32x4*>(
+                xs + (arow[rb] + (MY - 1 - ry) * WXP + (MX - 1 - rx)) * RSA + kofs);
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) Mma<TR>::step(acc[rb][cb], afr[rb], bfr[cb]);
+    };
     auto compute = [&](int st) __attribute__((always_inline)) {
         const S* xs = smem + st * C::STAGE;
         const S* bs = xs + C::XROWS * RSA;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const int kofs = ks * C::KSTEP + lg * VEC;
-            // one tap at a time: its CB B fragments once, then per shift class
-            // present its RB A fragments and the MFMAs of that class's blocks
 #pragma unroll
             for (int r = 0; r < T; ++r) {
-                u32x4 bfr[CB];
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
-                    bfr[cb] = *reinterpret_cast<const u32x4*>(
-                        bs + (r * BN + bcol + cb * 16) * RSA + kofs);
-#pragma unroll
-                for (int c = 0; c < (Y2 ? 4 : 2); ++c) {
-                    if (!(clsmask & (1u << c))) continue;
-                    const int ey = (c >> 1) + MY - 1 - r / MX;
-                    const int ex = (c & 1) + MX - 1 - r % MX;
-                    u32x4 afr[RB];
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-                        afr[rb] = *reinterpret_cast<const u32x4*>(
-                            xs + (arow[rb] + ey * WXP + ex) * RSA + kofs);
-#pragma unroll
-                    for (int cb = 0; cb < CB; ++cb)
-                        if (cls[cb] == c) {
-#pragma unroll
-                            for (int rb = 0; rb < RB; ++rb)
-                                Mma<TR>::step(acc[rb][cb], afr[rb], bfr[cb]);
-                        }
-                }
+                tap_step(xs, bs, ks * C::KSTEP + lg * VEC, r);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
     };
 
     // ---- main loop over input-channel chunks (two chunks per iteration) ----
-    // Waves whose column blocks all share one shift class (every wave of a
-    // shape whose phases split into classes along the wave boundaries) run a
-    // branch-free chunk step: per tap its A and B fragments and MFMAs, with the
-    // next chunk's global loads and the other stage's LDS stores issued right
-    // after the first tap so that they overlap the remaining MFMAs.
-    const bool single = (clsmask & (clsmask - 1u)) == 0u;
-    const int c0 = __builtin_ctz(clsmask);
-    int arow1[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) arow1[rb] = arow[rb] + (Y2 ? (c0 >> 1) * WXP : 0) + (c0 & 1);
-    // `pre` (the next chunk's global loads) is issued first and `mid` (the
-    // other stage's LDS stores, which wait for loads issued one step earlier)
-    // after the first tap; scheduling barriers keep the compiler from moving
-    // the loads late and their consumers early, which would expose the full
-    // memory latency at every step.
+    // The fused chunk step: the next chunk's global loads first, the other
+    // stage's LDS stores (which wait for loads issued one step earlier) right
+    // after the first tap, so that both overlap the remaining MFMAs;
+    // scheduling barriers keep the compiler from moving the loads late and
+    // their consumers early, which would expose the full memory latency at
+    // every step.
     auto fused = [&](int st, auto&& pre, auto&& mid) __attribute__((always_inline)) {
         const S* xs = smem + st * C::STAGE;
         const S* bs = xs + C::XROWS * RSA;
@@ -545,24 +504,9 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const int kofs = ks * C::KSTEP + lg * VEC;
 #pragma unroll
             for (int r = 0; r < T; ++r) {
-                const int ry = r / MX, rx = r % MX;
-                u32x4 afr[RB], bfr[CB];
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-                    afr[rb] = *reinterpret_cast<const u32x4*>(
-                        xs + (arow1[rb] + (MY - 1 - ry) * WXP + (MX - 1 - rx)) * RSA + kofs);
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
-                    bfr[cb] = *reinterpret_cast<const u32x4*>(
-                        bs + (r * BN + bcol + cb * 16) * RSA + kofs);
-#pragma unroll
-                for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-                        Mma<TR>::step(acc[rb][cb], afr[rb], bfr[cb]);
+                tap_step(xs, bs, ks * C::KSTEP + lg * VEC, r);
                 if (ks == 0 && r == 0) {
                     __builtin_amdgcn_sched_barrier(0);
                     mid();
@@ -582,7 +526,7 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
         const int c_last = c_end - 1;
         // (the fused step keeps both buffers and a tap's fragments live: only
         // instances with at most 8 B fragments per k-step fit without spills)
-        if (C::PF == 2 && CB * T <= 8 && single) {
+        if (C::PF == 2 && CB * T <= 8) {
             // two copies of the loop: with and without edge handling in the
             // LDS stores, so that the chunk step has no branch
             auto run = [&](auto inside) __attribute__((always_inline)) {
@@ -812,8 +756,11 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
         // them (one LDS latency per U stores).
         const int cpr = SS / VEC;
         const int total = nrows * cpr;
-        const int64_t ox0 = (int64_t)ax0 * a.sx;
-        const int lim = (int)min((int64_t)SS, a.Wo - ox0);  // valid elements of a row
+        // staged columns [lo, lim) of a row are real outputs (the padding
+        // shift makes the first tile's leading ones negative)
+        const int64_t ox0 = (int64_t)ax0 * a.sx - a.oxs;
+        const int lo = ox0 < 0 ? (int)(-ox0) : 0;
+        const int lim = (int)min((int64_t)SS, a.WoR - ox0);
         constexpr int U = 4;
         for (int e0 = tid; e0 < total; e0 += U * C::NT) {
             u32x4 v[U];
@@ -828,21 +775,23 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                 const int s0 = (ec - row * cpr) * VEC;
                 const int co_l = (int)fdiv((uint32_t)row, a.fd_R), rr = row - co_l * R;
                 const int co = co0 + co_l;
-                const int64_t oy = (int64_t)ay0 * a.sy + rr;
-                ok[u] = e < total && co < a.C_out && oy < a.Ho && s0 < lim;
+                const int64_t oy = (int64_t)ay0 * a.sy + rr - a.oys;
+                ok[u] = e < total && co < a.C_out && oy >= 0 && oy < a.HoR && s0 < lim &&
+                        s0 + VEC > lo;
                 sof[u] = co_l * CSTR + rr * SS;
                 s0v[u] = s0;
-                gb[u] = ((n * a.C_out + co) * a.Ho + oy) * a.Wo + ox0;
+                gb[u] = ((n * a.C_out + co) * a.HoR + oy) * a.WoR + ox0;
                 v[u] = *reinterpret_cast<const u32x4*>(smem + sof[u] + s0);
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 if (!ok[u]) continue;
                 const int s0 = s0v[u];
-                if (s0 + VEC <= lim) {
+                if (s0 >= lo && s0 + VEC <= lim) {
                     store16_unaligned(yg + gb[u] + s0, v[u]);
                 } else {
-                    for (int q = s0; q < lim; ++q) yg[gb[u] + q] = smem[sof[u] + q];
+                    const int qe = s0 + VEC < lim ? s0 + VEC : lim;
+                    for (int q = s0 < lo ? lo : s0; q < qe; ++q) yg[gb[u] + q] = smem[sof[u] + q];
                 }
             }
         }
@@ -852,40 +801,45 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
         const int co_l = (int)fdiv((uint32_t)row, a.fd_R), rr = row - co_l * R;
         const int co = co0 + co_l;
         if (co >= a.C_out) continue;
+        // output sizes of the padded problem (the dilation-reduced one under
+        // dilation); the staged indices are shifted back by the padding
+        const int64_t Hc = a.Ho - a.oys, Wc = a.Wo - a.oxs;
         int64_t oy, ox0;
-        int lim;  // valid elements of this staged row
+        int lo, lim;  // valid elements [lo, lim) of this staged row
         if (a.phase_subset) {
             oy = 0;
-            ox0 = (int64_t)(ax0 + rr) * a.sx + b0;
+            ox0 = (int64_t)(ax0 + rr) * a.sx + b0 - a.oxs;
             lim = min(SS, a.P - b0);
-            if (ox0 >= a.Wo) continue;
-            if (ox0 + lim > a.Wo) lim = (int)(a.Wo - ox0);
         } else {
-            oy = (int64_t)ay0 * a.sy + rr;
-            ox0 = (int64_t)ax0 * a.sx;
-            if (oy >= a.Ho || ox0 >= a.Wo) continue;
-            lim = (int)min((int64_t)SS, a.Wo - ox0);
+            oy = (int64_t)ay0 * a.sy + rr - a.oys;
+            ox0 = (int64_t)ax0 * a.sx - a.oxs;
+            if (oy < 0 || oy >= Hc) continue;
+            lim = SS;
         }
+        lo = ox0 < 0 ? (int)min((int64_t)lim, -ox0) : 0;
+        if (ox0 + lim > Wc) lim = (int)max((int64_t)0, Wc - ox0);
+        if (lim <= lo) continue;
         // staged (reduced) row -> real output row o0 + g * index per dimension
         const int64_t gbase =
             DIL ? ((n * a.C_out + co) * a.HoR + (a.o0y + a.gy * oy)) * a.WoR + a.o0x + a.gx * ox0
-                : ((n * a.C_out + co) * a.Ho + oy) * a.Wo + ox0;
+                : ((n * a.C_out + co) * a.HoR + oy) * a.WoR + ox0;
         const S* srow = smem + co_l * CSTR + rr * SS;
         if (vec_ok) {
             for (int s0 = lane * VEC; s0 < lim; s0 += 64 * VEC) {
-                if (s0 + VEC <= lim) {
+                if (s0 >= lo && s0 + VEC <= lim) {
                     store16_unaligned(yg + gbase + s0, *reinterpret_cast<const u32x4*>(srow + s0));
                 } else {
-                    for (int e = s0; e < lim; ++e) yg[gbase + e] = srow[e];
+                    const int ee = s0 + VEC < lim ? s0 + VEC : lim;
+                    for (int e = s0 < lo ? lo : s0; e < ee; ++e) yg[gbase + e] = srow[e];
                 }
             }
         } else {
             if (!DIL || a.gx == 1) {
-                for (int e = lane; e < lim; e += 64) yg[gbase + e] = srow[e];
+                for (int e = lo + lane; e < lim; e += 64) yg[gbase + e] = srow[e];
             } else if constexpr (DIL) {
                 // every gx-th output of the real row (dilation-reduced problem)
                 S* yrow = yg + gbase;
-                for (int e = lane; e < lim; e += 64) yrow[e * a.gx] = srow[e];
+                for (int e = lo + lane; e < lim; e += 64) yrow[e * a.gx] = srow[e];
             }
         }
     }
@@ -995,17 +949,16 @@ bool get_inst(const Problem& p, int CB, Inst* out) {
 
 constexpr int64_t kInt32Max = 2147483647;
 
-// Fill PolyArgs for problem p; false when no kernel instance covers it.
-// allow_split: the reduction may be split over workgroups (a workspace holds
-// the partial sums of all splits but the first).
+// Fill PolyArgs for problem p (no padding, no dilation); false when no
+// kernel instance covers it.  allow_split: the reduction may be split over
+// workgroups (a workspace holds the partial sums of all splits but the
+// first).
 bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allow_split) {
-    if (p.dH != 1 || p.dW != 1) return false;
+    if (p.dH != 1 || p.dW != 1 || p.pH != 0 || p.pW != 0) return false;
     if (p.H == 0 || p.W == 0 || p.N == 0) return false;
     // every staged x load covers 8 bytes of one input row
     if (p.W * (p.dtype == CTCONV_F32 ? 4 : 2) < 8) return false;
     const int64_t P = p.P;
-    const bool spread_y = (p.pH % p.sH) != 0, spread_x = (p.pW % p.sW) != 0;
-    const bool mixed_ok = !spread_y && !spread_x;  // delta_b is the same for every phase
 
     // Column tiling: TCO output channels x PT phases per tile.
     int CB = (p.ndim == 1 && P % 5 == 0 && P * 16 <= 160) ? 5 : 4;
@@ -1014,7 +967,7 @@ bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allo
     const int64_t BN = in.BN;
     int64_t TCO, PT;
     int subset = 0;
-    const bool narrow = (p.C_out < 16) && mixed_ok;  // blocks may span phases
+    const bool narrow = p.C_out < 16;  // blocks may span phases
     const int64_t tco_min = narrow ? p.C_out : 16;
     if (P * tco_min <= BN) {
         PT = P;
@@ -1063,18 +1016,12 @@ bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allo
     a->Wo = p.Wo;
     a->sy = (int)p.sH;
     a->sx = (int)p.sW;
-    a->py = (int)p.pH;
-    a->px = (int)p.pW;
     a->P = (int)P;
     a->T = (int)p.T;
     a->Ay = (int)Ay;
     a->Ax = (int)Ax;
-    a->dminy = (int)(p.pH / p.sH);
-    a->dminx = (int)(p.pW / p.sW);
-    a->spready = spread_y ? 1 : 0;
-    a->spreadx = spread_x ? 1 : 0;
-    a->WY = in.TAY + (int)p.mH - 1 + a->spready;
-    a->WX = in.TAX + (int)p.mW - 1 + a->spreadx;
+    a->WY = in.TAY + (int)p.mH - 1;
+    a->WX = in.TAX + (int)p.mW - 1;
     {
         // Rows a multiple of 4 bytes long start dword aligned (x itself is
         // 16-byte aligned), so a window start at a multiple of NP positions
@@ -1082,7 +1029,7 @@ bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allo
         // multiple of 8 bytes).  Tile starts are multiples of 16, so the
         // shift is the same for every tile.
         const int es = p.dtype == CTCONV_F32 ? 4 : 2, np = 8 / es;
-        const int w0 = a->dminx - ((int)p.mW - 1);
+        const int w0 = -((int)p.mW - 1);
         a->xofs = (p.W * es) % 4 == 0 ? ((w0 % np) + np) % np : 0;
     }
     a->TCO = (int)TCO;
@@ -1182,9 +1129,18 @@ bool reduce_dilation(const Problem& p, Problem* q, int* o0y, int* o0x) {
 bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allow_split) {
     Problem q;
     int o0y = 0, o0x = 0;
-    if (!reduce_dilation(p, &q, &o0y, &o0x)) return false;
-    if (q.Ho == 0 || q.Wo == 0) return false;
     const bool dilated = p.dH > 1 || p.dW > 1;
+    if (!reduce_dilation(p, &q, &o0y, &o0x)) return false;
+    // Padding as an output shift: output o of the padded problem is output
+    // o + p of the same transposed convolution without padding, so the kernel
+    // runs that one (outputs o' in [0, L_out + p)) and writes o' - p when it
+    // lies in [0, L_out).  Without padding output phase b reads inputs
+    // q - r for every phase alike (no phase-dependent input offset).
+    const int oys = (int)q.pH, oxs = (int)q.pW;
+    q.Ho += q.pH;
+    q.Wo += q.pW;
+    q.pH = q.pW = 0;
+    if (q.Ho == 0 || q.Wo == 0) return false;
     if (!plan_core(q, a, inst, splits, allow_split && !dilated)) return false;
     // dilation is compiled into the 3 x 3-tap 2-D instances only
     if ((p.dH > 1 || p.dW > 1) && !inst->dil) return false;
@@ -1200,6 +1156,9 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allow_spl
     a->o0x = o0x;
     a->HoR = p.Ho;
     a->WoR = p.Wo;
+    a->oys = oys;
+    a->oxs = oxs;
+    a->ws_slab = p.N * p.C_out * p.Ho * p.Wo;  // partial sums use y's own indexing
     a->psy = (int)p.sH;
     a->psx = (int)p.sW;
     a->pmx = (int)p.mW;
