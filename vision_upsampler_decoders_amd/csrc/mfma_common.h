@@ -53,6 +53,7 @@ struct Mma<TF32> {
 };
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_u __attribute__((ext_vector_type(2), aligned(1)));
 typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 
 // Fourth word of a raw (stride 0) buffer resource on gfx9-family chips:

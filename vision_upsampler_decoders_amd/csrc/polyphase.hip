@@ -147,6 +147,24 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     const int wm = wave / WN, wn = wave % WN;
     const int li = lane & 15, lg = lane >> 4;
 
+    // Column tc of the tile -> (phase pb within the tile, output channel
+    // co_l within the tile).  Channel-major: TCO channels of phase 0, then of
+    // phase 1, ...  Phase-fastest (pfast): 16-column blocks cycle through the
+    // PT phases of one 16-channel group before the next group, so that a wave
+    // holds whole runs of consecutive phases of its channels (stored straight
+    // from registers).  co_l >= TCO marks a padding block.
+    auto col_map = [&](int tc, int& pb, int& co_l) __attribute__((always_inline)) {
+        if (a.pfast) {
+            const int blk = tc >> 4;
+            const int g = (int)fdiv((uint32_t)blk, a.fd_pt);
+            pb = blk - g * a.PT;
+            co_l = g * 16 + (tc & 15);
+        } else {
+            pb = (int)fdiv((uint32_t)tc, a.fd_tco);
+            co_l = tc - pb * a.TCO;
+        }
+    };
+
     // ---- x staging descriptors: item = (window row, NP positions, VEC channels)
     // Each channel of an item is one 8-byte global load (NP positions); the
     // VEC x NP block is transposed in registers into NP LDS rows of VEC
@@ -259,9 +277,10 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
         if (qw < bper && q < C::BMAX) {
             const int row = q / NG, piece = q % NG;
             const int r = row / BN, tc = row % BN;
-            const int pb = (int)fdiv((uint32_t)tc, a.fd_tco);
-            const int co = co0 + tc - pb * a.TCO, b = b0 + pb;
-            if (pb < a.PT && b < a.P && co < a.C_out) {
+            int pb, co_l;
+            col_map(tc, pb, co_l);
+            const int co = co0 + co_l, b = b0 + pb;
+            if (pb < a.PT && b < a.P && co_l < a.TCO && co < a.C_out) {
                 const int by = (int)fdiv((uint32_t)b, a.fd_sx), bx = b - by * a.sx;
                 // without padding, output phase b is weight phase b
                 const int jy = by, jx = bx;
@@ -447,9 +466,11 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
             const int tc = bcol + cb * 16;
-            const int pb = (int)fdiv((uint32_t)tc, a.fd_tco);
-            const int co = co0 + tc - pb * a.TCO;
-            const uint32_t off = (pb < a.PT && co < a.C_out) ? (uint32_t)co * C::ES : 0x7FFFFFF0u;
+            int pb, co_l;
+            col_map(tc, pb, co_l);
+            const int co = co0 + co_l;
+            const uint32_t off =
+                (pb < a.PT && co_l < a.TCO && co < a.C_out) ? (uint32_t)co * C::ES : 0x7FFFFFF0u;
             if constexpr (C::ES == 2)
                 bvs[cb] = TR::to_f32(__builtin_amdgcn_raw_buffer_load_b16(bres, off, 0, 0));
             else
@@ -702,7 +723,94 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                 }
             }
         };
-        if (!a.phase_subset && (a.TCO & 15) == 0 && a.TCO / 16 == 1) {
+        // Phase-fastest columns: the blocks of a wave are consecutive phases
+        // of one 16-channel group, so for each of its row blocks a lane holds
+        // runs of consecutive staged elements of one channel row:
+        //  - whole rows of phases (sx phases b_x of output row b_y): the 4
+        //    rows q (MFMA rows 4 lg .. 4 lg + 3) times sx phases are 4 sx
+        //    consecutive elements;
+        //  - CB consecutive phases of a longer row (sx > CB): CB consecutive
+        //    elements per row q.
+        // Each run is rounded and written with 8- or 16-byte LDS stores (the
+        // run starts are 8-byte aligned: the channel stride is a multiple of
+        // 16 bytes and a run starts at a multiple of 4 sx, or of CB, elements).
+        auto stage_runs = [&](auto sx_tag) __attribute__((always_inline)) {
+            constexpr int SXC = decltype(sx_tag)::value;  // 0: runs of CB phases per row q
+            constexpr int STEP = SXC > 0 ? SXC : CB;
+            constexpr int L = SXC > 0 ? 4 * SXC : CB;     // elements per run
+            static_assert(sizeof(S) == 4 || L % 4 == 0 || SXC % 2 == 1, "run shape");
+            auto put = [&](const float* v, int off) __attribute__((always_inline)) {
+                S* d = smem + off;
+                if constexpr (sizeof(S) == 2) {
+                    uint32_t w[(L + 1) / 2];
+#pragma unroll
+                    for (int e = 0; e < L / 2; ++e) w[e] = pack2<TR>(v[2 * e], v[2 * e + 1]);
+                    if constexpr (L % 2 == 1) w[L / 2] = (uint32_t)TR::from_f32(v[L - 1]);
+                    if constexpr (SXC % 2 == 0 && SXC > 0) {
+                        // 16-byte aligned runs of 8 or 16 elements
+#pragma unroll
+                        for (int e = 0; e < L / 2; e += 4)
+                            *reinterpret_cast<u32x4*>(d + 2 * e) = u32x4{w[e], w[e + 1], w[e + 2], w[e + 3]};
+                    } else {
+#pragma unroll
+                        for (int e = 0; e + 2 <= L / 2; e += 2)
+                            *reinterpret_cast<u32x2*>(d + 2 * e) = u32x2{w[e], w[e + 1]};
+                        if constexpr ((L / 2) % 2 == 1)
+                            *reinterpret_cast<uint32_t*>(d + L - 2) = w[L / 2 - 1];
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e + 2 <= L; e += 2)
+                        *reinterpret_cast<u32x2*>(d + e) = u32x2{__float_as_uint(v[e]), __float_as_uint(v[e + 1])};
+                    if constexpr (L % 2 == 1) d[L - 1] = v[L - 1];
+                }
+            };
+#pragma unroll
+            for (int cb0 = 0; cb0 < CB; cb0 += STEP) {
+                const int blk = wn * CB + cb0;
+                const int g = (int)uniform(fdiv((uint32_t)blk, a.fd_pt));
+                const int pb = blk - g * a.PT;
+                if (g * 16 >= a.TCO) continue;  // padding blocks
+                const int by = (int)uniform(fdiv((uint32_t)pb, a.fd_sx)), bx0 = pb - by * a.sx;
+                const int chan = (g * 16 + li) * CSTR;
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const int t0 = (wm * RB + rb) * 16 + 4 * lg;
+                    const int rr = (t0 / TAX) * a.sy + by, tx0 = t0 % TAX;
+                    if constexpr (SXC > 0) {
+                        float v[L];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+#pragma unroll
+                            for (int bx = 0; bx < SXC; ++bx)
+                                v[i * SXC + bx] = actf(acc[rb][cb0 + bx][i] + bvs[cb0 + bx]);
+                        put(v, chan + rr * SS + tx0 * SXC);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            float v[L];
+#pragma unroll
+                            for (int j = 0; j < CB; ++j) v[j] = actf(acc[rb][j][i] + bvs[j]);
+                            put(v, chan + rr * SS + (tx0 + i) * a.sx + bx0);
+                        }
+                    }
+                }
+            }
+        };
+        if (a.pfast) {
+            // the planner sets pfast only for the layouts handled here
+            if (a.sx > CB) {
+                if constexpr (sizeof(S) == 4 || CB % 4 == 0) stage_runs(std::integral_constant<int, 0>{});
+            } else if (a.sx == 1) {
+                stage_runs(std::integral_constant<int, 1>{});
+            } else if (a.sx == 2) {
+                if constexpr (CB % 2 == 0) stage_runs(std::integral_constant<int, 2>{});
+            } else if (a.sx == 4) {
+                if constexpr (CB % 4 == 0) stage_runs(std::integral_constant<int, 4>{});
+            } else if (a.sx == 5) {
+                if constexpr (CB % 5 == 0) stage_runs(std::integral_constant<int, 5>{});
+            }
+        } else if (!a.phase_subset && (a.TCO & 15) == 0 && a.TCO / 16 == 1) {
             stage_pairs(std::integral_constant<int, 1>{});
         } else if (!a.phase_subset && (a.TCO & 15) == 0 && a.TCO / 16 == 2) {
             stage_pairs(std::integral_constant<int, 2>{});
@@ -855,6 +963,7 @@ struct Inst {
     KernelFn fn;
     int BM, BN, TAX, TAY, KC, threads, lds_bytes;
     bool dil;  // runs dilation-reduced problems
+    int cb;    // 16-column blocks per wave
 };
 
 template <class TR, int MY, int MX, int TAX, int RB, int CB, int WM, int WN, int KS,
@@ -862,7 +971,7 @@ template <class TR, int MY, int MX, int TAX, int RB, int CB, int WM, int WN, int
 Inst make_inst() {
     using C = Cfg<TR, MY, MX, TAX, RB, CB, WM, WN, KS>;
     return Inst{&poly_kernel<TR, MY, MX, TAX, RB, CB, WM, WN, KS, XODD, DIL>, C::BM, C::BN, TAX,
-                C::TAY, C::KC, C::NT, (int)(C::SMEM * C::ES), DIL};
+                C::TAY, C::KC, C::NT, (int)(C::SMEM * C::ES), DIL, CB};
 }
 
 // Tile shapes.  16-bit storage, 1-D with one or two taps: 128 output rows x
@@ -1035,6 +1144,24 @@ bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allo
     a->TCO = (int)TCO;
     a->PT = (int)PT;
     a->phase_subset = subset;
+    {
+        // phase-fastest columns and run staging of the epilogue, for the
+        // layouts it handles: every phase in the tile, 16-channel groups, no
+        // dilation instance, staged rows a whole number of 16-byte chunks
+        // (the flattened stores) and per wave either whole output rows of
+        // phases (sx dividing CB) or CB consecutive phases of a row
+        const int cb = in.cb;
+        const int64_t sx = p.sW;
+        const bool es2 = p.dtype != CTCONV_F32;
+        const bool rows = (sx == 1 || sx == 2 || sx == 4 || sx == 5) && sx <= cb && cb % sx == 0 &&
+                          (cb % P == 0 || P % cb == 0);
+        const bool part = sx > cb && sx % cb == 0 && P % cb == 0 && (!es2 || cb % 4 == 0);
+        const int64_t vec = es2 ? 8 : 4;
+        a->pfast = (!subset && !narrow && TCO % 16 == 0 && PT == P && !in.dil &&
+                    (in.TAX * sx) % vec == 0 && (rows || part))
+                       ? 1 : 0;
+        a->fd_pt = make_fastdiv((uint32_t)PT);
+    }
     a->n_ph_tiles = (int)n_ph_tiles;
     a->n_col_tiles = (int)n_col_tiles;
     a->tiles_y = (int)tiles_y;

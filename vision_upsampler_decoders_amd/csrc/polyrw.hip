@@ -62,7 +62,6 @@ constexpr int RW_LDS_MAX = 65536;               // dynamic LDS per workgroup (by
 constexpr int RW_NBUF = 2;
 constexpr int RW_THREADS = 64 * RW_WAVES;
 
-typedef uint32_t u32x2_u __attribute__((ext_vector_type(2), aligned(1)));
 
 struct RWArgs {
     const void* x;
