@@ -135,7 +135,7 @@ def test_forward_validation_before_launch(lib):
     assert _fwd(lib, y=0x3008) == 5
     assert _fwd(lib, b=0x4004) == 5
     # polyphase forced on a shape outside the polyphase form
-    assert _fwd(lib, d=2, k=4, s=3, route=1) == 3    # dilation not dividing the stride
+    assert _fwd(lib, d=3, k=5, s=2, route=1) == 3    # 7 expanded taps per phase: no instance
     assert _fwd(lib, d=2, k=9, s=2, route=1) == 3    # reduced problem with 9 taps
     assert _fwd(lib, k=20, s=4, p=2, route=1) == 3   # 5 taps per phase
     assert _fwd(lib, sp=(3,), dt=1, route=1) == 3     # rows shorter than 8 bytes
@@ -174,26 +174,39 @@ def test_routes_of_workloads(lib, name, route):
 
 @pytest.mark.parametrize("k,s,p,op,d,route", [
     (8, 4, 2, 0, 1, 1), (6, 3, 0, 0, 1, 1), (4, 1, 1, 0, 1, 1), (3, 2, 1, 0, 1, 1),
-    (8, 4, 2, 1, 1, 1), (8, 4, 2, 0, 2, 2), (16, 4, 2, 0, 1, 1), (20, 4, 2, 0, 1, 2),
+    (8, 4, 2, 1, 1, 1), (16, 4, 2, 0, 1, 1), (20, 4, 2, 0, 1, 2),
     (7, 3, 2, 2, 1, 1), (13, 4, 1, 0, 1, 1), (17, 4, 1, 0, 1, 2),
-    (3, 2, 1, 1, 2, 2), (4, 4, 1, 0, 2, 2), (5, 2, 1, 0, 3, 2),
+    # dilation: g = gcd(s, d), s' = s / g, d' = d / g, expanded kernel of
+    # (k - 1) d' + 1 taps, m = ceil(that / s')
+    (8, 4, 2, 0, 2, 1),   # g 2, s' 2, d' 1: m 4
+    (3, 2, 1, 1, 2, 1),   # g 2, s' 1: m 3
+    (4, 4, 1, 0, 2, 1),   # g 2, s' 2: m 2
+    (3, 2, 1, 0, 3, 1),   # g 1, d' 3: 7 taps, m 4
+    (4, 3, 1, 0, 2, 1),   # g 1, d' 2: 7 taps, m 3
+    (3, 4, 1, 0, 6, 1),   # g 2, s' 2, d' 3: 7 taps, m 4
+    (5, 2, 1, 0, 3, 2),   # g 1, d' 3: 13 taps, m 7
+    (4, 2, 1, 0, 3, 2),   # g 1, d' 3: 10 taps, m 5
 ])
 def test_route_rule(lib, k, s, p, op, d, route):
-    # 1-D: polyphase iff d == 1 and m = ceil(k / s) within the compiled taps
+    # 1-D: polyphase iff the taps per phase (of the dilation-expanded kernel
+    # at the reduced stride) are within the compiled 1 .. 4
     assert C.ctconv_query_route(2, 16, 16, (50,), k, s, p, op, d, 1) == route
 
 
 @pytest.mark.parametrize("k,s,p,op,d,route", [
     ((3, 3), (2, 2), (1, 1), (1, 1), (2, 2), 1),   # reduced: stride 1, 3 x 3 taps
-    ((3, 3), (4, 4), (1, 1), (0, 0), (2, 2), 2),   # reduced: stride 2, 2 x 2 taps
-    ((3, 3), (3, 3), (1, 1), (0, 0), (2, 2), 2),   # d does not divide s
+    ((3, 3), (4, 4), (1, 1), (0, 0), (2, 2), 1),   # reduced: stride 2, 2 x 2 taps
+    ((3, 3), (3, 3), (1, 1), (0, 0), (2, 2), 2),   # 9 phases: more than a 2-D tile holds
+    ((3, 2), (3, 1), (1, 0), (2, 0), (2, 1), 1),   # y expanded: 5 taps at stride 3, 2 x 2
+    ((3, 3), (2, 2), (1, 1), (0, 0), (3, 3), 2),   # expanded: 7 taps at stride 2, 4 x 4
+    ((4, 2), (2, 2), (1, 2), (0, 1), (1, 3), 1),   # x expanded to 4 taps: 2 x 2
     ((3, 3), (1, 1), (1, 1), (0, 0), (1, 1), 1),   # 3 x 3 taps without dilation
     ((5, 5), (2, 2), (2, 2), (1, 1), (1, 1), 1),   # 3 x 3 taps per phase
 ])
 def test_route_rule_2d_dilation(lib, k, s, p, op, d, route):
-    # 2-D: dilation d dividing s reduces to stride s / d with
-    # m = ceil(k / (s / d)) taps per dimension; the instances that run a
-    # reduced problem are the 3 x 3-tap ones
+    # 2-D: per dimension reduction by gcd(s, d) and expansion of the rest of
+    # the dilation; the compiled 2-D tap counts are 1 or 2 per dimension, or
+    # 3 x 3
     assert C.ctconv_query_route(2, 16, 16, (20, 22), k, s, p, op, d, 0) == route
 
 

@@ -147,14 +147,23 @@ FULL_CASES = [
     ("s5_m3_op2_bf16", "bf16", 2, 72, 40, (257,), (13,), (5,), (4,), (2,), (1,), True),
     ("s5_m4_f16", "f16", 1, 40, 30, (300,), (20,), (5,), (7,), (0,), (1,), False),
     ("s4_m4_bf16", "bf16", 2, 64, 48, (400,), (16,), (4,), (6,), (0,), (1,), True),
-    # dilation dividing the stride: 2-D 3 x 3 reduced taps on the polyphase
-    # route (the reduced problem of stride s / d; every other output is the
-    # bias) in fp32 and in 16-bit with odd rows; 1-D on the gather route
+    # dilation on the polyphase route: reduction by g = gcd(s, d) (the
+    # problem of stride s / g; outputs off the g-grid are the bias) and
+    # expansion of the remaining d / g into zero taps; 2-D 3 x 3 reduced taps
+    # in fp32 and in 16-bit with odd rows, 1-D reductions, 1-D and 2-D
+    # expansions, and both at once
     ("dil2_s2_2d_f32", "f32", 1, 24, 20, (13, 17), (3, 3), (2, 2), (1, 1), (1, 1), (2, 2), True),
     ("dil2_s2_2d_bf16_odd", "bf16", 1, 40, 24, (9, 11), (3, 3), (2, 2), (0, 1), (0, 1), (2, 2),
      True),
     ("dil2_s4_bf16", "bf16", 2, 40, 24, (101,), (8,), (4,), (3,), (1,), (2,), True),
     ("dil3_s3_k4_f16", "f16", 2, 33, 17, (90,), (4,), (3,), (2,), (2,), (3,), False),
+    ("dil3_s2_k3_bf16", "bf16", 2, 48, 40, (203,), (3,), (2,), (1,), (0,), (3,), True),
+    ("dil2_s3_k4_f32", "f32", 2, 40, 24, (150,), (4,), (3,), (2,), (1,), (2,), True),
+    ("dil6_s4_k3_bf16", "bf16", 1, 64, 48, (120,), (3,), (4,), (5,), (2,), (6,), True),
+    ("dil2_s4_2d_f32", "f32", 1, 24, 20, (13, 17), (3, 3), (4, 4), (1, 2), (0, 1), (2, 2), True),
+    ("dilx3_s2_2d_bf16", "bf16", 1, 40, 24, (11, 19), (4, 2), (2, 2), (1, 2), (0, 1), (1, 3),
+     True),
+    ("dil2_s3x1_2d_f16", "f16", 1, 36, 20, (10, 12), (3, 2), (3, 1), (1, 0), (2, 0), (2, 1), False),
 ]
 
 

@@ -120,9 +120,12 @@ ctconv_status build_problem(int64_t N, int64_t C_in, int64_t C_out, int ndim,
 
 bool polyphase_eligible(const Problem& p) {
     // Any k: with m = ceil(k / s) taps per phase the packed weight's taps past
-    // k are zero; output_padding only lengthens the output.  Dilation when it
-    // divides the stride (the kernel runs the reduced problem of stride s / d).
-    return (p.dH == 1 || p.sH % p.dH == 0) && (p.dW == 1 || p.sW % p.dW == 0);
+    // k are zero; output_padding only lengthens the output.  Any dilation: the
+    // kernel runs the problem reduced by gcd(s, d) with the remaining
+    // dilation expanded into zero taps (the planner declines tap counts no
+    // kernel instance covers).
+    (void)p;
+    return true;
 }
 
 ctconv_route choose_route(const Problem& p) {

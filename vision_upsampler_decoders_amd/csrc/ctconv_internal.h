@@ -153,11 +153,15 @@ struct PolyArgs {
     int xcd_remap;         // 1: gridDim.x is a multiple of 8, remap for L2 locality
     uint32_t pw_bytes;     // size of the packed weight (below 2^32)
     int act;               // ctconv_activation of the epilogue
-    // Dilation d dividing s (per dimension): the kernel runs the reduced
-    // problem (stride s/d, dilation 1) whose output u' sits at o0 + g*u' of
-    // the real output (g = d); the other outputs are bias only (pre-filled).
-    // Identity (g = 1, o0 = 0, real sizes = Ho, Wo) without dilation.
+    // Dilation (per dimension): the kernel runs the problem reduced by
+    // g = gcd(s, d) (stride s/g), whose output u' sits at o0 + g*u' of the
+    // real output; the other outputs are bias only (pre-filled).  Identity
+    // (g = 1, o0 = 0, real sizes = Ho, Wo) when g = 1.
     int gy, gx, o0y, o0x;
+    // Remaining dilation d' = d / g: the kernel's taps are the expanded
+    // kernel's, real tap e / d' where d' divides e (1 without dilation)
+    int dey, dex;
+    FastDiv fd_dey, fd_dex;
     int64_t HoR, WoR;      // real output sizes (addressing of y)
     // Padding as an output shift: the kernel computes the transposed
     // convolution without padding (of the dilation-reduced problem under
@@ -165,8 +169,8 @@ struct PolyArgs {
     // when it lies inside, i.e. below Ho - os (Wo - os)
     int oys, oxs;
     // Packed-weight geometry (the real stride and taps the weight was packed
-    // with): effective tap (s_e*r + j) per dimension is real tap t, stored as
-    // phase t mod ps, tap t / ps; taps t >= k read as zero.
+    // with): the kernel's tap e = s' r + j per dimension is real tap t = e / d',
+    // stored as phase t mod ps, tap t / ps; other taps and t >= k read as zero.
     int psy, psx, pmx, pT, kH, kW;
     uint32_t pw_cblock;    // bytes of one 32-channel block of a phase (C_out * pT * 32)
 };

@@ -106,8 +106,7 @@ struct Cfg {
 // 2-byte-misaligned 8-byte load costs the texture path per lane).
 // At least two waves per SIMD (256 registers per wave): an 8-wave workgroup
 // per CU, or two 4-wave ones; only 128 x 128 wave tiles need the whole file.
-template <class TR, int MY, int MX, int TAX, int RB, int CB, int WM, int WN, int KS, bool XODD,
-          bool DIL>
+template <class TR, int MY, int MX, int TAX, int RB, int CB, int WM, int WN, int KS, bool XODD>
 __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_kernel(
     const PolyArgs a) {
     using C = Cfg<TR, MY, MX, TAX, RB, CB, WM, WN, KS>;
@@ -282,32 +281,29 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
             const int co = co0 + co_l, b = b0 + pb;
             if (pb < a.PT && b < a.P && co_l < a.TCO && co < a.C_out) {
                 const int by = (int)fdiv((uint32_t)b, a.fd_sx), bx = b - by * a.sx;
-                // without padding, output phase b is weight phase b
-                const int jy = by, jx = bx;
-                if (!DIL || (a.gy == 1 && a.gx == 1)) {
-                    // packed layout [j][ci / 32][co][r][ci % 32]: row (co, r)
-                    // of phase j in channel block 0 (the chunk adds its block)
-                    boff[it] = (uint32_t)(((((int64_t)(jy * a.sx + jx) * (a.C_in_pad / kCinAlign) *
-                                                 a.C_out + co) * T + r) * kCinAlign +
-                                           piece * VEC) * C::ES);
-                } else if constexpr (DIL) {
-                    // dilation-reduced problem: its tap (ry, rx) of weight phase
-                    // (jy, jx) is real tap (ty, tx), packed as phase (ty mod psy,
-                    // tx mod psx), tap (ty / psy, tx / psx); taps past k read as
-                    // zero (an offset past the packed weight, which is below
-                    // 2^31 bytes: the range check of the load returns zeros)
-                    const int ty = a.sy * (r / MX) + jy, tx = a.sx * (r % MX) + jx;
-                    if (ty < a.kH && tx < a.kW) {
-                        const int qy = (int)fdiv((uint32_t)ty, a.fd_psy);
-                        const int qx = (int)fdiv((uint32_t)tx, a.fd_psx);
-                        const int jp = (ty - qy * a.psy) * a.psx + (tx - qx * a.psx);
-                        const int rp = qy * a.pmx + qx;
-                        boff[it] = (uint32_t)((((int64_t)jp * (a.C_in_pad / kCinAlign) * a.C_out +
-                                                co) * a.pT + rp) * kCinAlign + piece * VEC) *
-                                   C::ES;
-                    } else {
-                        boff[it] = 0x80000000u;
-                    }
+                const int jy = by, jx = bx;  // (kernel phase = output phase)
+                // Kernel tap (ry, rx) of kernel phase (jy, jx) is tap e = s' r + j
+                // of the kernel the kernel runs (per dimension: stride s' and
+                // the real taps spread d' apart, d' = 1 without dilation).  A
+                // real tap t = e / d' exists when d' divides e and t < k; the
+                // packed weight holds it as phase t mod s, tap t / s of the
+                // real stride s.  Missing taps read as zero (an offset past the
+                // packed weight, which is below 2^31 bytes: the range check of
+                // the load returns zeros).
+                const int ey = a.sy * (r / MX) + jy, ex = a.sx * (r % MX) + jx;
+                const int ty = (int)fdiv((uint32_t)ey, a.fd_dey), tx = (int)fdiv((uint32_t)ex, a.fd_dex);
+                if (ty * a.dey == ey && tx * a.dex == ex && ty < a.kH && tx < a.kW) {
+                    const int qy = (int)fdiv((uint32_t)ty, a.fd_psy);
+                    const int qx = (int)fdiv((uint32_t)tx, a.fd_psx);
+                    const int jp = (ty - qy * a.psy) * a.psx + (tx - qx * a.psx);
+                    const int rp = qy * a.pmx + qx;
+                    // packed layout [j][ci / 32][co][t][ci % 32]: row (co, t) of
+                    // phase j in channel block 0 (the chunk adds its block)
+                    boff[it] = (uint32_t)((((int64_t)jp * (a.C_in_pad / kCinAlign) * a.C_out + co) *
+                                               a.pT + rp) * kCinAlign + piece * VEC) *
+                               C::ES;
+                } else {
+                    boff[it] = 0x80000000u;
                 }
             }
             blds[it] = (r * BN + tc) * RSA + piece * VEC;
@@ -354,12 +350,9 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
             }
         // the chunk's channel block (a column tile's rows of one block are
         // contiguous) and its offset inside the block
-        uint32_t bchunk;
-        if constexpr (DIL)  // (the packed weight's taps, not the kernel's)
-            bchunk = uniform((cbase / kCinAlign) * a.pw_cblock + (cbase % kCinAlign) * C::ES);
-        else
-            bchunk = uniform(((cbase / kCinAlign) * (uint32_t)(a.C_out * T) * kCinAlign +
-                              cbase % kCinAlign) * C::ES);
+        // (blocks of the packed weight's taps, not the kernel's)
+        const uint32_t bchunk =
+            uniform((cbase / kCinAlign) * a.pw_cblock + (cbase % kCinAlign) * C::ES);
 #pragma unroll
         for (int it = 0; it < C::BITEMS; ++it)
             br[it] = __builtin_bit_cast(
@@ -855,7 +848,7 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                              : static_cast<S*>(a.y);
     const int nrows = a.TCO * R;
     // (a dilation-reduced problem writes every g-th output: element stores)
-    const bool vec_ok = (SS % VEC) == 0 && (!DIL || (a.gx == 1 && a.gy == 1));
+    const bool vec_ok = (SS % VEC) == 0 && a.gx == 1 && a.gy == 1;
     if (vec_ok && !a.phase_subset) {
         // Flattened over the tile: chunk e (VEC elements) is row e / cpr,
         // column chunk e % cpr of the staged output, so consecutive lanes
@@ -929,8 +922,7 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
         if (lim <= lo) continue;
         // staged (reduced) row -> real output row o0 + g * index per dimension
         const int64_t gbase =
-            DIL ? ((n * a.C_out + co) * a.HoR + (a.o0y + a.gy * oy)) * a.WoR + a.o0x + a.gx * ox0
-                : ((n * a.C_out + co) * a.HoR + oy) * a.WoR + ox0;
+            ((n * a.C_out + co) * a.HoR + (a.o0y + a.gy * oy)) * a.WoR + a.o0x + a.gx * ox0;
         const S* srow = smem + co_l * CSTR + rr * SS;
         if (vec_ok) {
             for (int s0 = lane * VEC; s0 < lim; s0 += 64 * VEC) {
@@ -942,9 +934,9 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                 }
             }
         } else {
-            if (!DIL || a.gx == 1) {
+            if (a.gx == 1) {
                 for (int e = lo + lane; e < lim; e += 64) yg[gbase + e] = srow[e];
-            } else if constexpr (DIL) {
+            } else {
                 // every gx-th output of the real row (dilation-reduced problem)
                 S* yrow = yg + gbase;
                 for (int e = lo + lane; e < lim; e += 64) yrow[e * a.gx] = srow[e];
@@ -962,16 +954,15 @@ using KernelFn = void (*)(const PolyArgs);
 struct Inst {
     KernelFn fn;
     int BM, BN, TAX, TAY, KC, threads, lds_bytes;
-    bool dil;  // runs dilation-reduced problems
-    int cb;    // 16-column blocks per wave
+    int cb;  // 16-column blocks per wave
 };
 
 template <class TR, int MY, int MX, int TAX, int RB, int CB, int WM, int WN, int KS,
-          bool XODD = false, bool DIL = false>
+          bool XODD = false>
 Inst make_inst() {
     using C = Cfg<TR, MY, MX, TAX, RB, CB, WM, WN, KS>;
-    return Inst{&poly_kernel<TR, MY, MX, TAX, RB, CB, WM, WN, KS, XODD, DIL>, C::BM, C::BN, TAX,
-                C::TAY, C::KC, C::NT, (int)(C::SMEM * C::ES), DIL, CB};
+    return Inst{&poly_kernel<TR, MY, MX, TAX, RB, CB, WM, WN, KS, XODD>, C::BM, C::BN, TAX,
+                C::TAY, C::KC, C::NT, (int)(C::SMEM * C::ES), CB};
 }
 
 // Tile shapes.  16-bit storage, 1-D with one or two taps: 128 output rows x
@@ -1031,7 +1022,7 @@ bool pick_inst_x(const Problem& p, int CB, Inst* out) {
     // 128 x 64 tiles, eight waves of 64 x 16, so that two stages of nine
     // taps' weight rows fit in LDS
     if (p.mH == 3 && p.mW == 3) {
-        *out = make_inst<TR, 3, 3, 32, 4, 1, 2, 4, 1, XO, true>();
+        *out = make_inst<TR, 3, 3, 32, 4, 1, 2, 4, 1, XO>();
         return true;
     }
     return false;
@@ -1146,8 +1137,8 @@ bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allo
     a->phase_subset = subset;
     {
         // phase-fastest columns and run staging of the epilogue, for the
-        // layouts it handles: every phase in the tile, 16-channel groups, no
-        // dilation instance, staged rows a whole number of 16-byte chunks
+        // layouts it handles: every phase in the tile, 16-channel groups,
+        // staged rows a whole number of 16-byte chunks
         // (the flattened stores) and per wave either whole output rows of
         // phases (sx dividing CB) or CB consecutive phases of a row
         const int cb = in.cb;
@@ -1157,7 +1148,7 @@ bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allo
                           (cb % P == 0 || P % cb == 0);
         const bool part = sx > cb && sx % cb == 0 && P % cb == 0 && (!es2 || cb % 4 == 0);
         const int64_t vec = es2 ? 8 : 4;
-        a->pfast = (!subset && !narrow && TCO % 16 == 0 && PT == P && !in.dil &&
+        a->pfast = (!subset && !narrow && TCO % 16 == 0 && PT == P &&
                     (in.TAX * sx) % vec == 0 && (rows || part))
                        ? 1 : 0;
         a->fd_pt = make_fastdiv((uint32_t)PT);
@@ -1220,44 +1211,78 @@ bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allo
     return true;
 }
 
-// Dilation d dividing s, per dimension.  Output o receives a tap only when
-// o + p is a multiple of d (i*s - p + t*d = o with d | s); those outputs,
-// u = (o + p) / d, form the transposed convolution with stride s / d,
-// dilation 1 and the same taps.  Counting them from the first one,
-// o0 = (d - p mod d) mod d, gives u' = (o - o0) / d and left padding
-// u0 = (o0 + p) / d.  Without dilation the problem is returned unchanged.
-bool reduce_dilation(const Problem& p, Problem* q, int* o0y, int* o0x) {
-    *q = p;
-    *o0y = 0;
-    *o0x = 0;
+// Dilation, per dimension, in two steps.
+//  1. Reduction by g = gcd(s, d): output o = i s - p + t d receives a tap
+//     only when g divides o + p.  Those outputs, u = (o + p) / g, form the
+//     transposed convolution with stride s' = s / g and dilation d' = d / g.
+//     Counting them from the first one, o0 = (g - p mod g) mod g, gives
+//     u' = (o - o0) / g and left padding (o0 + p) / g; the other outputs hold
+//     the bias alone.
+//  2. Expansion of the remaining dilation d' (coprime to s'): the kernel runs
+//     the undilated transposed convolution whose kernel has (k - 1) d' + 1
+//     taps, tap e being real tap e / d' when d' divides e and zero otherwise
+//     (the kernel reads the packed weight through that map).
+// Without dilation the problem is returned unchanged (g = d' = 1).
+struct Reduced {
+    Problem q;    // the problem the kernel runs (dilation 1)
+    int g[2];     // output step per dimension (y, x)
+    int o0[2];    // first reached output per dimension
+    int de[2];    // tap spacing d' of the expanded kernel per dimension
+};
+
+int64_t gcd64(int64_t a, int64_t b) {
+    while (b) {
+        const int64_t t = a % b;
+        a = b;
+        b = t;
+    }
+    return a;
+}
+
+bool reduce_dilation(const Problem& p, Reduced* r) {
+    r->q = p;
     auto one = [](int64_t d, int64_t s, int64_t pad, int64_t L, int64_t k, int64_t* s2,
-                  int64_t* pad2, int64_t* L2, int64_t* m2, int* o0) {
+                  int64_t* pad2, int64_t* L2, int64_t* k2, int64_t* m2, int* g_out, int* o0,
+                  int* de) {
+        *g_out = 1;
+        *o0 = 0;
+        *de = 1;
         if (d == 1) return true;
-        if (d < 1 || s % d != 0) return false;
-        const int64_t first = (d - pad % d) % d;
+        if (d < 1 || s < 1 || k < 1) return false;
+        const int64_t g = gcd64(s, d);
+        const int64_t first = (g - pad % g) % g;
+        *g_out = (int)g;
         *o0 = (int)first;
-        *s2 = s / d;
-        *pad2 = (first + pad) / d;
-        *L2 = L > first ? (L - first + d - 1) / d : 0;
-        *m2 = (k + *s2 - 1) / *s2;
+        *de = (int)(d / g);
+        *s2 = s / g;
+        *pad2 = (first + pad) / g;
+        *L2 = L > first ? (L - first + g - 1) / g : 0;
+        *k2 = (k - 1) * (d / g) + 1;
+        *m2 = (*k2 + *s2 - 1) / *s2;
         return true;
     };
-    if (!one(p.dH, p.sH, p.pH, p.Ho, p.kH, &q->sH, &q->pH, &q->Ho, &q->mH, o0y)) return false;
-    if (!one(p.dW, p.sW, p.pW, p.Wo, p.kW, &q->sW, &q->pW, &q->Wo, &q->mW, o0x)) return false;
-    q->dH = q->dW = 1;
-    q->opH = q->opW = 0;  // the reduced output sizes are set directly
-    q->P = q->sH * q->sW;
-    q->T = q->mH * q->mW;
+    Problem& q = r->q;
+    if (!one(p.dH, p.sH, p.pH, p.Ho, p.kH, &q.sH, &q.pH, &q.Ho, &q.kH, &q.mH, &r->g[0], &r->o0[0],
+             &r->de[0]))
+        return false;
+    if (!one(p.dW, p.sW, p.pW, p.Wo, p.kW, &q.sW, &q.pW, &q.Wo, &q.kW, &q.mW, &r->g[1], &r->o0[1],
+             &r->de[1]))
+        return false;
+    q.dH = q.dW = 1;
+    q.opH = q.opW = 0;  // the reduced output sizes are set directly
+    q.P = q.sH * q.sW;
+    q.T = q.mH * q.mW;
     return true;
 }
 
-// Fill PolyArgs for problem p (any dilation that divides the stride).  A
-// dilated problem is never split (its untouched outputs hold the bias).
+// Fill PolyArgs for problem p (any dilation).  A problem with a reduction
+// step (g > 1) is never split (its unreached outputs hold the pre-filled
+// bias, which a split's partial sums would overwrite).
 bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allow_split) {
-    Problem q;
-    int o0y = 0, o0x = 0;
-    const bool dilated = p.dH > 1 || p.dW > 1;
-    if (!reduce_dilation(p, &q, &o0y, &o0x)) return false;
+    Reduced rd;
+    if (!reduce_dilation(p, &rd)) return false;
+    Problem& q = rd.q;
+    const bool reduced = rd.g[0] > 1 || rd.g[1] > 1;
     // Padding as an output shift: output o of the padded problem is output
     // o + p of the same transposed convolution without padding, so the kernel
     // runs that one (outputs o' in [0, L_out + p)) and writes o' - p when it
@@ -1268,23 +1293,28 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allow_spl
     q.Wo += q.pW;
     q.pH = q.pW = 0;
     if (q.Ho == 0 || q.Wo == 0) return false;
-    if (!plan_core(q, a, inst, splits, allow_split && !dilated)) return false;
-    // dilation is compiled into the 3 x 3-tap 2-D instances only
-    if ((p.dH > 1 || p.dW > 1) && !inst->dil) return false;
+    if (!plan_core(q, a, inst, splits, allow_split && !reduced)) return false;
     // the packed weight is the real one: its size, strides and taps
     const int64_t pw_bytes = p.P * p.C_out * p.T * p.C_in_pad * (p.dtype == CTCONV_F32 ? 4 : 2);
     // (an offset of 2^31 must lie past it: taps past k read as zero)
     if (pw_bytes >= (int64_t)0x80000000LL) return false;
     if (p.Ho > kInt32Max / 2 || p.Wo > kInt32Max / 2) return false;
     a->pw_bytes = (uint32_t)pw_bytes;
-    a->gy = (int)p.dH;
-    a->gx = (int)p.dW;
-    a->o0y = o0y;
-    a->o0x = o0x;
+    a->gy = rd.g[0];
+    a->gx = rd.g[1];
+    a->o0y = rd.o0[0];
+    a->o0x = rd.o0[1];
+    a->dey = rd.de[0];
+    a->dex = rd.de[1];
+    a->fd_dey = make_fastdiv((uint32_t)rd.de[0]);
+    a->fd_dex = make_fastdiv((uint32_t)rd.de[1]);
     a->HoR = p.Ho;
     a->WoR = p.Wo;
     a->oys = oys;
     a->oxs = oxs;
+    // the run staging writes every output of its tile in order: only where
+    // every output is reached (no reduction step)
+    if (reduced) a->pfast = 0;
     a->ws_slab = p.N * p.C_out * p.Ho * p.Wo;  // partial sums use y's own indexing
     a->psy = (int)p.sH;
     a->psx = (int)p.sW;
