@@ -122,10 +122,16 @@ struct PolyArgs {
     const void* bias;
     void* y;
     int64_t N, C_in, C_out, C_in_pad;
-    int64_t H, W, Ho, Wo;  // Ho, Wo: outputs of the padding-free problem run
-    int sy, sx;
+    int64_t H, W, Ho, Wo;  // Ho, Wo: outputs of the problem the kernel runs
+    int sy, sx, py, px;    // its stride and padding (padding 0 unless cmode)
     int P, T;
     int Ay, Ax;            // output rows per dimension in units of the stride
+    // Class mode (cmode = 1): phase rows aligned to the output under padding
+    // p; output phase b reads input rows from floor((b + p) / s) on, i.e.
+    // dmin = floor(p / s) plus 0 or 1 per phase and dimension, and each column
+    // block reads its own A fragments.  Without it the planner has removed
+    // the padding (dmin = 0, every phase alike).
+    int cmode, dminy, dminx;
     int WY, WX;            // x window per tile (rows x columns)
     int xofs;              // window start moved back by this many positions so
                            // that every x load is 8-byte aligned (0 when rows

@@ -73,11 +73,15 @@ struct Cfg {
     static constexpr int BN = WN * CB * 16;
     static constexpr int TAY = BM / TAX;
     static constexpr int T = MY * MX;
-    static constexpr int WYM = TAY + MY - 1;  // window rows
+    // window rows: the tile, the halo and (2-D, output-aligned phase rows
+    // under padding) one more row for the phases whose inputs start a row
+    // later
+    static constexpr int WYM = TAY + MY - 1 + (TAY > 1 ? 1 : 0);
     static constexpr int NP = 8 / ES;                             // positions per load item
-    // window columns: the tile, the halo and up to NP-1 positions of
-    // alignment shift, padded to whole fragments
-    static constexpr int WXP = (TAX + MX - 1 + NP - 1 + VEC - 1) / VEC * VEC;
+    // window columns: the tile, the halo, one more column for output-aligned
+    // phase rows under padding and up to NP-1 positions of alignment shift,
+    // padded to whole fragments
+    static constexpr int WXP = (TAX + MX + NP - 1 + VEC - 1) / VEC * VEC;
     static constexpr int XROWS = WYM * WXP;
     static constexpr int BROWS = T * BN;
     static constexpr int STAGE = (XROWS + BROWS) * RSA;
@@ -137,10 +141,12 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     const int co0 = cq * a.TCO;
     const int b0 = (col_tile - cq * a.n_ph_tiles) * a.PT;
     const int ay0 = ty_t * C::TAY, ax0 = tx_t * TAX;
-    // output phase row q takes input rows q - r, r < m: the window starts
-    // m - 1 rows before the tile
-    const int wy0 = ay0 - (MY - 1);
-    const int wx0 = ax0 - (MX - 1) - a.xofs;
+    // output phase row q takes input rows q + delta_b - r, r < m (delta_b = 0
+    // for every phase unless the phase rows are output-aligned under
+    // padding): the window starts m - 1 rows before the tile's smallest
+    // delta
+    const int wy0 = ay0 + a.dminy - (MY - 1);
+    const int wx0 = ax0 + a.dminx - (MX - 1) - a.xofs;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
@@ -281,7 +287,10 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
             const int co = co0 + co_l, b = b0 + pb;
             if (pb < a.PT && b < a.P && co_l < a.TCO && co < a.C_out) {
                 const int by = (int)fdiv((uint32_t)b, a.fd_sx), bx = b - by * a.sx;
-                const int jy = by, jx = bx;  // (kernel phase = output phase)
+                // weight phase of output phase b: (b + p) mod s (b itself
+                // without padding)
+                const int jy = by + a.py - (int)fdiv((uint32_t)(by + a.py), a.fd_sy) * a.sy;
+                const int jx = bx + a.px - (int)fdiv((uint32_t)(bx + a.px), a.fd_sx) * a.sx;
                 // Kernel tap (ry, rx) of kernel phase (jy, jx) is tap e = s' r + j
                 // of the kernel the kernel runs (per dimension: stride s' and
                 // the real taps spread d' apart, d' = 1 without dilation).  A
@@ -476,12 +485,60 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     // q takes input q - r) and the MFMAs of every (row block, column block)
     // pair.  A scheduling barrier between taps keeps one tap's fragments live
     // at a time.
+    // Output-aligned phase rows (class mode): column block cb holds one phase
+    // b whose input rows start delta_b = floor((b + p) / s) - floor(p / s)
+    // (0 or 1 per dimension) later; its A fragments sit that much further in
+    // the window.  Wave-uniform element offsets, 0 outside class mode.
+    int cofs[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+        int o = 0;
+        if (C::TAY > 1 && a.cmode) {
+            int pb, co_l;
+            col_map(wn * CB * 16 + cb * 16, pb, co_l);
+            const int b = b0 + (pb < a.PT ? pb : 0);
+            const int by = (int)fdiv((uint32_t)b, a.fd_sx), bx = b - by * a.sx;
+            const int dy = (int)fdiv((uint32_t)(by + a.py), a.fd_sy) - a.dminy;
+            const int dx = (int)fdiv((uint32_t)(bx + a.px), a.fd_sx) - a.dminx;
+            o = (dy * WXP + dx) * RSA;
+        }
+        cofs[cb] = (int)uniform((uint32_t)o);
+    }
+    // (class mode) window row of row block rb relative to row block 0: the
+    // wave's rows start at a tile-row boundary or stay inside one tile row
+    static_assert(C::TAY == 1 || (RB * 16) % TAX == 0 || TAX % (RB * 16) == 0, "row blocks");
+    auto rb_row_offset = [](int rb) constexpr {
+        return (RB * 16) % TAX == 0 ? ((rb * 16) / TAX) * WXP + (rb * 16) % TAX : rb * 16;
+    };
+    int abase[CB];
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) abase[cb] = arow[0] * RSA + cofs[cb];
     auto tap_step = [&](const S* xs, const S* bs, int kofs, int r) __attribute__((always_inline)) {
         const int ry = r / MX, rx = r % MX;
         u32x4 afr[RB], bfr[CB];
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb)
             bfr[cb] = *reinterpret_cast<const u32x4*>(bs + (r * BN + bcol + cb * 16) * RSA + kofs);
+        if constexpr (C::TAY > 1) {
+            if (a.cmode) {
+                // every (row block, column block) pair reads its own A
+                // fragment: one address register per column block, the row
+                // block and the tap in the instruction's offset; one row
+                // block's fragments live at a time
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const int rofs = (rb_row_offset(rb) + (MY - 1 - ry) * WXP + (MX - 1 - rx)) * RSA;
+                    u32x4 af[CB];
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb)
+                        af[cb] = *reinterpret_cast<const u32x4*>(xs + abase[cb] + rofs + kofs);
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) Mma<TR>::step(acc[rb][cb], af[cb], bfr[cb]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                return;
+            }
+        }
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
             afr[rb] = *reinterpret_cast<const u32x4*>(
@@ -1049,12 +1106,15 @@ bool get_inst(const Problem& p, int CB, Inst* out) {
 
 constexpr int64_t kInt32Max = 2147483647;
 
-// Fill PolyArgs for problem p (no padding, no dilation); false when no
-// kernel instance covers it.  allow_split: the reduction may be split over
-// workgroups (a workspace holds the partial sums of all splits but the
-// first).
-bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allow_split) {
-    if (p.dH != 1 || p.dW != 1 || p.pH != 0 || p.pW != 0) return false;
+// Fill PolyArgs for problem p (no dilation; no padding unless cmode); false
+// when no kernel instance covers it.  cmode: phase rows aligned to the
+// output, each 16-column block one phase with its own input offset.
+// allow_split: the reduction may be split over workgroups (a workspace holds
+// the partial sums of all splits but the first).
+bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allow_split,
+               bool cmode) {
+    if (p.dH != 1 || p.dW != 1) return false;
+    if (!cmode && (p.pH != 0 || p.pW != 0)) return false;
     if (p.H == 0 || p.W == 0 || p.N == 0) return false;
     // every staged x load covers 8 bytes of one input row
     if (p.W * (p.dtype == CTCONV_F32 ? 4 : 2) < 8) return false;
@@ -1086,6 +1146,13 @@ bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allo
         if (!narrow) PT = PT / 1;  // 16-channel blocks, one phase each
     }
     if (TCO < 1 || PT < 1) return false;
+    // class mode reads A fragments per 16-column block: one phase per block;
+    // compiled into the 2-D instances only (1-D shapes lose at most one tile
+    // per batch item to the padding shift)
+    if (cmode && (narrow || subset || in.TAY == 1)) return false;
+    const int spready = cmode && p.pH % p.sH != 0 ? 1 : 0;
+    const int spreadx = cmode && p.pW % p.sW != 0 ? 1 : 0;
+    if (spready && in.TAY == 1) return false;  // (1-D tiles have one window row)
     const int64_t n_co_tiles = (p.C_out + TCO - 1) / TCO;
     const int64_t n_ph_tiles = (P + PT - 1) / PT;
     const int64_t Ay = (p.Ho + p.sH - 1) / p.sH, Ax = (p.Wo + p.sW - 1) / p.sW;
@@ -1116,12 +1183,17 @@ bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allo
     a->Wo = p.Wo;
     a->sy = (int)p.sH;
     a->sx = (int)p.sW;
+    a->py = (int)p.pH;
+    a->px = (int)p.pW;
+    a->cmode = cmode ? 1 : 0;
+    a->dminy = (int)(p.pH / p.sH);
+    a->dminx = (int)(p.pW / p.sW);
     a->P = (int)P;
     a->T = (int)p.T;
     a->Ay = (int)Ay;
     a->Ax = (int)Ax;
-    a->WY = in.TAY + (int)p.mH - 1;
-    a->WX = in.TAX + (int)p.mW - 1;
+    a->WY = in.TAY + (int)p.mH - 1 + spready;
+    a->WX = in.TAX + (int)p.mW - 1 + spreadx;
     {
         // Rows a multiple of 4 bytes long start dword aligned (x itself is
         // 16-byte aligned), so a window start at a multiple of NP positions
@@ -1129,7 +1201,7 @@ bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allo
         // multiple of 8 bytes).  Tile starts are multiples of 16, so the
         // shift is the same for every tile.
         const int es = p.dtype == CTCONV_F32 ? 4 : 2, np = 8 / es;
-        const int w0 = -((int)p.mW - 1);
+        const int w0 = a->dminx - ((int)p.mW - 1);
         a->xofs = (p.W * es) % 4 == 0 ? ((w0 % np) + np) % np : 0;
     }
     a->TCO = (int)TCO;
@@ -1288,12 +1360,35 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allow_spl
     // runs that one (outputs o' in [0, L_out + p)) and writes o' - p when it
     // lies in [0, L_out).  Without padding output phase b reads inputs
     // q - r for every phase alike (no phase-dependent input offset).
-    const int oys = (int)q.pH, oxs = (int)q.pW;
-    q.Ho += q.pH;
-    q.Wo += q.pW;
-    q.pH = q.pW = 0;
-    if (q.Ho == 0 || q.Wo == 0) return false;
-    if (!plan_core(q, a, inst, splits, allow_split && !reduced)) return false;
+    // When that adds a phase row or column that costs a whole extra tile row
+    // or column (a tile dimension the phase rows fit exactly), class mode
+    // keeps output-aligned phase rows instead: the phases then read inputs
+    // from different offsets, each 16-column block its own.
+    Problem qs = q;
+    qs.Ho += qs.pH;
+    qs.Wo += qs.pW;
+    qs.pH = qs.pW = 0;
+    if (qs.Ho == 0 || qs.Wo == 0) return false;
+    bool cmode = false;
+    if (q.pH % q.sH != 0 || q.pW % q.sW != 0) {
+        PolyArgs ac{};
+        Inst ic{};
+        int spc = 1;
+        if (plan_core(qs, a, inst, splits, false, false) && q.Ho > 0 && q.Wo > 0 &&
+            plan_core(q, &ac, &ic, &spc, false, true)) {
+            const double ts = (double)a->n_tiles, tc = (double)ac.n_tiles;
+            cmode = ts > 1.1 * tc;
+        }
+    }
+    int oys = 0, oxs = 0;
+    if (cmode) {
+        if (!plan_core(q, a, inst, splits, allow_split && !reduced, true)) return false;
+    } else {
+        oys = (int)q.pH;
+        oxs = (int)q.pW;
+        q = qs;
+        if (!plan_core(q, a, inst, splits, allow_split && !reduced, false)) return false;
+    }
     // the packed weight is the real one: its size, strides and taps
     const int64_t pw_bytes = p.P * p.C_out * p.T * p.C_in_pad * (p.dtype == CTCONV_F32 ? 4 : 2);
     // (an offset of 2^31 must lie past it: taps past k read as zero)
