@@ -138,7 +138,9 @@ struct PolyArgs {
                            // are not a multiple of 8 bytes)
     int TCO, PT;           // output channels and phases per column tile
     int phase_subset;      // 0: a column tile holds every phase; 1: a run of PT phases
-    int pfast;             // 1: phase-fastest column order, epilogue staged in runs
+    int pfast;             // column order: 0 channel-major, 1 phase-fastest, 2 row-phase-
+                           // fastest (class mode, sx = 2); 1 and 2 stage the epilogue in runs
+    
     int n_ph_tiles, n_col_tiles;
     int tiles_y, tiles_x;
     int64_t n_row_tiles;
@@ -147,7 +149,7 @@ struct PolyArgs {
     // tile channels, strides, staged output rows and their 16-byte chunks)
     FastDiv fd_cols, fd_ph, fd_tx, fd_ty, fd_wy, fd_tco, fd_sx, fd_sy, fd_R;
     FastDiv fd_cpr;        // 16-byte chunks per staged output row
-    FastDiv fd_pt;         // phases per column tile
+    FastDiv fd_pt;         // blocks per cycle of the column order: PT (pfast 1), 2 TCO/16 (pfast 2)
     FastDiv fd_psy, fd_psx;  // strides of the packed weight
     int n_chunks;          // C_in_pad / KC
     int chunks_per_split;  // split over C_in: each blockIdx.y takes this many chunks

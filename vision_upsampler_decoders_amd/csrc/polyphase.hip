@@ -158,12 +158,22 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     // PT phases of one 16-channel group before the next group, so that a wave
     // holds whole runs of consecutive phases of its channels (stored straight
     // from registers).  co_l >= TCO marks a padding block.
+    // Row-phase-fastest (pfast = 2, class mode with two phases per output
+    // row): blocks cycle through the 2 phases b_x of one output row b_y, then
+    // the next 16-channel group, then the next row, so that block cb's phase
+    // b_x is cb mod 2 and a wave's blocks share b_y.
     auto col_map = [&](int tc, int& pb, int& co_l) __attribute__((always_inline)) {
-        if (a.pfast) {
+        if (a.pfast == 1) {
             const int blk = tc >> 4;
             const int g = (int)fdiv((uint32_t)blk, a.fd_pt);
             pb = blk - g * a.PT;
             co_l = g * 16 + (tc & 15);
+        } else if (a.pfast == 2) {
+            const int blk = tc >> 4;
+            const int by = (int)fdiv((uint32_t)blk, a.fd_pt);  // fd_pt: 2 TCO / 16
+            const int rem = blk - by * (2 * (a.TCO >> 4));
+            pb = by * 2 + (rem & 1);
+            co_l = (rem >> 1) * 16 + (tc & 15);
         } else {
             pb = (int)fdiv((uint32_t)tc, a.fd_tco);
             co_l = tc - pb * a.TCO;
@@ -521,6 +531,24 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
             bfr[cb] = *reinterpret_cast<const u32x4*>(bs + (r * BN + bcol + cb * 16) * RSA + kofs);
         if constexpr (C::TAY > 1) {
             if (a.cmode) {
+                if constexpr (CB % 2 == 0) {
+                    if (a.pfast == 2) {
+                        // blocks of even and odd cb are the two phases of one
+                        // output row: two A fragments per row block
+#pragma unroll
+                        for (int rb = 0; rb < RB; ++rb) {
+                            const int rofs =
+                                (rb_row_offset(rb) + (MY - 1 - ry) * WXP + (MX - 1 - rx)) * RSA;
+                            const u32x4 a0 = *reinterpret_cast<const u32x4*>(xs + abase[0] + rofs + kofs);
+                            const u32x4 a1 = *reinterpret_cast<const u32x4*>(xs + abase[1] + rofs + kofs);
+#pragma unroll
+                            for (int cb = 0; cb < CB; ++cb)
+                                Mma<TR>::step(acc[rb][cb], (cb & 1) ? a1 : a0, bfr[cb]);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        return;
+                    }
+                }
                 // every (row block, column block) pair reads its own A
                 // fragment: one address register per column block, the row
                 // block and the tap in the instruction's offset; one row
@@ -817,12 +845,13 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
             };
 #pragma unroll
             for (int cb0 = 0; cb0 < CB; cb0 += STEP) {
-                const int blk = wn * CB + cb0;
-                const int g = (int)uniform(fdiv((uint32_t)blk, a.fd_pt));
-                const int pb = blk - g * a.PT;
-                if (g * 16 >= a.TCO) continue;  // padding blocks
+                int pb, co_b;
+                col_map((wn * CB + cb0) * 16, pb, co_b);
+                pb = (int)uniform((uint32_t)pb);
+                co_b = (int)uniform((uint32_t)co_b);
+                if (co_b >= a.TCO || pb >= a.PT) continue;  // padding blocks
                 const int by = (int)uniform(fdiv((uint32_t)pb, a.fd_sx)), bx0 = pb - by * a.sx;
-                const int chan = (g * 16 + li) * CSTR;
+                const int chan = (co_b + li) * CSTR;
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
                     const int t0 = (wm * RB + rb) * 16 + 4 * lg;
@@ -1383,6 +1412,14 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allow_spl
     int oys = 0, oxs = 0;
     if (cmode) {
         if (!plan_core(q, a, inst, splits, allow_split && !reduced, true)) return false;
+        // two phases per output row and whole rows of (2 phases x channel
+        // groups) per wave: row-phase-fastest columns (blocks share A
+        // fragments by phase parity; the epilogue still stages runs)
+        const int64_t groups = a->TCO / 16;
+        if (a->pfast == 1 && q.sW == 2 && inst->cb % 2 == 0 && (2 * groups) % inst->cb == 0) {
+            a->pfast = 2;
+            a->fd_pt = make_fastdiv((uint32_t)(2 * groups));
+        }
     } else {
         oys = (int)q.pH;
         oxs = (int)q.pW;
