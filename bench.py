@@ -32,6 +32,9 @@ sys.path.insert(0, ROOT)
 METRIC = "ConvTranspose TFLOP/s (2*N*Cin*Cout*K*Lin) and % of MFMA/HBM roofline, 1 GPU"
 PEAK_MFMA = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # dense TFLOP/s
 PEAK_HBM = 8000.0  # GB/s
+# fp32 vector arithmetic (the gather kernel's FMAs, every dtype): 256 CUs x
+# 4 SIMDs x 16 lanes x 2 FMA per lane (packed) x 2 flop x 2.4 GHz
+PEAK_ALU = 157.3  # TFLOP/s
 FLUSH_BYTES = 512 << 20  # larger than the 256 MB MALL
 ESIZE = {"f32": 4, "bf16": 2, "f16": 2}
 
@@ -426,6 +429,7 @@ def main():
     value = total_flops / (wall / args.steps) / 1e12
 
     layers = []
+    t_roof = 0.0
     for li, (L, sp, osp, fl, nb) in enumerate(geo):
         t = layer_ms[li] * 1e-3
         if L.groups > 1:
@@ -435,8 +439,12 @@ def main():
         else:
             route = C.ctconv_query_route(wl.N, L.C_in, L.C_out, sp, L.kernel, L.stride,
                                          L.padding, L.output_padding, L.dilation, dcode)
-        t_mfma = fl / (PEAK_MFMA[wl.dtype] * 1e12)
+        # compute peak of the layer's kernel: MFMA for the polyphase and
+        # depthwise kernels, fp32 vector ALU for the gather kernel
+        alu = route == 2
+        t_mfma = fl / ((PEAK_ALU if alu else PEAK_MFMA[wl.dtype]) * 1e12)
         t_hbm = nb / (PEAK_HBM * 1e9)
+        t_roof += max(t_mfma, t_hbm)
         layers.append({
             "layer": li, "C_in": L.C_in, "C_out": L.C_out, "kernel": list(L.kernel),
             "stride": list(L.stride), "in": list(sp), "out": list(osp),
@@ -447,7 +455,7 @@ def main():
             "us_cold_p10_p50_p90": pcts(cold_layer_samples[li]),
             "workspace_bytes": int(wspaces[li].numel()) if wspaces[li] is not None else 0,
             "tflops": round(fl / t / 1e12, 2), "gbps": round(nb / t / 1e9, 1),
-            "bound": "mfma" if t_mfma >= t_hbm else "hbm",
+            "bound": ("alu" if alu else "mfma") if t_mfma >= t_hbm else "hbm",
             "frac_roofline": round(max(t_mfma, t_hbm) / t, 4),
             "frac_mfma": round(t_mfma / t, 4), "frac_hbm": round(t_hbm / t, 4),
         })
@@ -457,9 +465,10 @@ def main():
     Ld = layers[dom]
     fl_d, nb_d = geo[dom][3], geo[dom][4]
     t_d = layer_ms[dom] * 1e-3
-    if Ld["bound"] == "mfma":
-        roof = {"bound": "mfma", "achieved": round(fl_d / t_d / 1e12, 2),
-                "peak": PEAK_MFMA[wl.dtype], "unit": "TFLOP/s"}
+    if Ld["bound"] in ("mfma", "alu"):
+        roof = {"bound": Ld["bound"], "achieved": round(fl_d / t_d / 1e12, 2),
+                "peak": PEAK_ALU if Ld["bound"] == "alu" else PEAK_MFMA[wl.dtype],
+                "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": round(nb_d / t_d / 1e9, 1), "peak": PEAK_HBM,
                 "unit": "GB/s"}
@@ -470,12 +479,11 @@ def main():
     roof["avg_launch_us"] = Ld["us"]
     # the same launch after a cache flush (median over the cold reps)
     t_c = float(np.median(cold_layer_samples[dom])) * 1e-3
-    ach_c = fl_d / t_c / 1e12 if roof["bound"] == "mfma" else nb_d / t_c / 1e9
-    roof["cold"] = {"achieved": round(ach_c, 2 if roof["bound"] == "mfma" else 1),
+    ach_c = fl_d / t_c / 1e12 if roof["bound"] != "hbm" else nb_d / t_c / 1e9
+    roof["cold"] = {"achieved": round(ach_c, 2 if roof["bound"] != "hbm" else 1),
                     "frac": round(ach_c / roof["peak"], 4), "median_launch_us": round(t_c * 1e6, 2),
                     "reps": cold_reps}
 
-    t_roof = sum(max(g[3] / (PEAK_MFMA[wl.dtype] * 1e12), g[4] / (PEAK_HBM * 1e9)) for g in geo)
 
     res = {
         "metric": METRIC,

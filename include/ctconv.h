@@ -309,14 +309,14 @@ ctconv_status ctconv_istft_normalize(const void* y, const void* env, void* out, 
  * Concatenating the y of successive ctconv_stream_step calls and then the y
  * of ctconv_stream_flush gives the one-shot transposed convolution of all the
  * frames with padding 0 (length (F - 1)*s + k), with the bias and the
- * activation applied once to every output.  The tail is kept as fp32 partial
- * sums without bias; products are accumulated in fp32 within a chunk, and a
- * chunk's conv output is rounded to dtype once before the tail is added.
+ * activation applied once to every output.  The chunk's conv output and the
+ * tail are kept as fp32 partial sums without bias; each output is rounded to
+ * dtype exactly once, after the tail and the bias are added.
  *
  * ctconv_stream_sizes (host only): for a chunk of L_chunk frames, *y_len =
  * L_chunk * s outputs per row, *tail_len = k - s (0 if k <= s) tail values per
- * row, *workspace_bytes = N * C_out * (L_chunk*s + tail_len) * sizeof(dtype)
- * for the chunk's conv output (0 when L_chunk = 0).
+ * row, *workspace_bytes = N * C_out * (L_chunk*s + tail_len) * 4 for the
+ * chunk's fp32 conv output (0 when L_chunk = 0).
  *
  * ctconv_stream_step: one chunk.
  *   x          device [N, C_in, L_chunk], L_chunk >= 1 frames

@@ -223,9 +223,10 @@ def test_route_short_rows(lib, sp, dt, route):
 
 def test_stream_sizes(lib):
     # chunk of L frames: L*s outputs, k - s tail values, conv workspace
-    assert C.ctconv_stream_sizes(2, 3, 5, 10, 5, 1) == (25, 5, 2 * 3 * 30 * 2)
+    # (the chunk's conv output is fp32 in every dtype)
+    assert C.ctconv_stream_sizes(2, 3, 5, 10, 5, 1) == (25, 5, 2 * 3 * 30 * 4)
     assert C.ctconv_stream_sizes(1, 4, 2, 16, 4, 0) == (8, 12, 1 * 4 * 20 * 4)
-    assert C.ctconv_stream_sizes(1, 4, 3, 4, 4, 2) == (12, 0, 1 * 4 * 12 * 2)
+    assert C.ctconv_stream_sizes(1, 4, 3, 4, 4, 2) == (12, 0, 1 * 4 * 12 * 4)
     assert C.ctconv_stream_sizes(1, 4, 0, 8, 4, 1) == (0, 4, 0)
 
 

@@ -263,7 +263,7 @@ ctconv_status forward_impl(const void* x, const void* packed_w, const void* bias
     if (route == CTCONV_ROUTE_AUTO) route = choose_route(p);
     if (route == CTCONV_ROUTE_POLYPHASE) route = polyphase_kernel(p);
     if (route == CTCONV_ROUTE_POLYPHASE_STREAM)
-        return to_status(launch_polyrw(p, x, packed_w, bias, y, s));
+        return to_status(launch_polyrw(p, x, packed_w, bias, y, false, s));
     if (route == CTCONV_ROUTE_POLYPHASE_TILED) {
         if (ws_call) {
             const size_t need = polyphase_workspace_bytes(p);
@@ -274,7 +274,7 @@ ctconv_status forward_impl(const void* x, const void* packed_w, const void* bias
         }
         return to_status(launch_polyphase(p, x, packed_w, bias, y, ws, ws_bytes, s));
     }
-    return to_status(launch_gather(p, x, packed_w, bias, y, s));
+    return to_status(launch_gather(p, x, packed_w, bias, y, false, s));
 }
 
 }  // namespace
@@ -354,7 +354,8 @@ ctconv_status stream_geometry(int64_t N, int64_t C_out, int64_t L, int64_t k, in
     if (!mul_ok(L, s, &ly)) return CTCONV_ERR_SHAPE;
     const int64_t tl = k > s ? k - s : 0;
     if (ly > kI64Max - tl) return CTCONV_ERR_SHAPE;
-    if (!mul_ok(N, C_out, &t) || !mul_ok(t, ly + tl, &t) || !mul_ok(t, (int64_t)esize(dt), &t))
+    // the chunk's conv output is kept in fp32 (rounded once, when emitted)
+    if (!mul_ok(N, C_out, &t) || !mul_ok(t, ly + tl, &t) || !mul_ok(t, (int64_t)sizeof(float), &t))
         return CTCONV_ERR_SHAPE;
     *Ly = ly;
     *Tl = tl;
@@ -391,15 +392,30 @@ ctconv_status ctconv_stream_step(const void* x, const void* packed_w, const void
         (bias && !aligned16(bias)) || (tail_in && !aligned16(tail_in)) ||
         (tail_out && !aligned16(tail_out)))
         return CTCONV_ERR_ALIGN;
-    // z = convT(chunk) with padding 0 and no bias, into the workspace
+    // z = convT(chunk) with padding 0 and no bias, in fp32, into the
+    // workspace: fp32 inputs through the ordinary forward; 16-bit inputs
+    // through the register-weight streaming kernel where it applies, else the
+    // gather kernel, both writing their fp32 accumulators unrounded
     const int64_t one = 1, zero = 0;
-    st = ctconv_forward_act(x, packed_w, nullptr, workspace, N, C_in, C_out, 1, &L_chunk, &kernel,
-                            &stride, &zero, &zero, &one, dtype, CTCONV_ACT_NONE,
-                            CTCONV_ROUTE_AUTO, stream);
-    if (st != CTCONV_OK) return st;
-    return to_status(launch_stream_overlap(workspace, tail_in, bias, y, tail_out, N * C_out, C_out,
-                                           Ly, Tl, dtype, (int)act,
-                                           static_cast<hipStream_t>(stream)));
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (dtype == CTCONV_F32) {
+        st = ctconv_forward_act(x, packed_w, nullptr, workspace, N, C_in, C_out, 1, &L_chunk,
+                                &kernel, &stride, &zero, &zero, &one, dtype, CTCONV_ACT_NONE,
+                                CTCONV_ROUTE_AUTO, stream);
+        if (st != CTCONV_OK) return st;
+    } else {
+        Problem p;
+        st = build_problem(N, C_in, C_out, 1, &L_chunk, &kernel, &stride, &zero, &zero, &one,
+                           dtype, &p);
+        if (st != CTCONV_OK) return st;
+        p.act = CTCONV_ACT_NONE;
+        const hipError_t e = polyrw_supported(p)
+                                 ? launch_polyrw(p, x, packed_w, nullptr, workspace, true, hs)
+                                 : launch_gather(p, x, packed_w, nullptr, workspace, true, hs);
+        if (e != hipSuccess) return to_status(e);
+    }
+    return to_status(launch_stream_overlap(static_cast<const float*>(workspace), tail_in, bias, y,
+                                           tail_out, N * C_out, C_out, Ly, Tl, dtype, (int)act, hs));
 }
 
 ctconv_status ctconv_stream_flush(const float* tail_in, const void* bias, void* y, int64_t N,

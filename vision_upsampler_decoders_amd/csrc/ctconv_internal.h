@@ -186,7 +186,9 @@ struct PolyArgs {
 // Launchers (each returns hipGetLastError() of its launch).
 hipError_t launch_prepack(const Problem& p, const void* w, void* pw, hipStream_t s);
 hipError_t launch_gather(const Problem& p, const void* x, const void* pw, const void* bias,
-                         void* y, hipStream_t s);
+                         void* y, bool out_f32, hipStream_t s);
+// the staged gather kernel covers p (else the general one runs)
+bool gather_staged_ok(const Problem& p);
 hipError_t launch_fill(const Problem& p, const void* bias, void* y, hipStream_t s);
 // y = act(y + ws[0] + ... + ws[nslab-1] + bias), fp32, added in that order.
 hipError_t launch_split_reduce(const Problem& p, const void* bias, void* y, const void* ws,
@@ -198,7 +200,7 @@ hipError_t launch_istft_norm(const void* y, const void* env, void* out, int64_t 
 
 // Streaming overlap-add and flush (rows = N * C_out; Ly emitted outputs and
 // Tl tail values per row).
-hipError_t launch_stream_overlap(const void* z, const float* tail_in, const void* bias, void* y,
+hipError_t launch_stream_overlap(const float* z, const float* tail_in, const void* bias, void* y,
                                  float* tail_out, int64_t rows, int64_t C_out, int64_t Ly,
                                  int64_t Tl, ctconv_dtype dt, int act, hipStream_t s);
 hipError_t launch_stream_flush(const float* tail_in, const void* bias, void* y, int64_t rows,
@@ -225,7 +227,7 @@ size_t polyphase_workspace_bytes(const Problem& p);
 // taps x padded input channels <= 256): never splits, needs no workspace.
 bool polyrw_supported(const Problem& p);
 hipError_t launch_polyrw(const Problem& p, const void* x, const void* pw, const void* bias,
-                         void* y, hipStream_t s);
+                         void* y, bool out_f32, hipStream_t s);
 hipError_t launch_polyphase(const Problem& p, const void* x, const void* pw, const void* bias,
                             void* y, void* ws, size_t ws_bytes, hipStream_t s);
 

@@ -83,6 +83,7 @@ struct RWArgs {
     uint32_t img;       // bytes of one image (C_in * plane)
     uint32_t pw_bytes;
     int act;
+    int outf32;         // 1: y is fp32 (no rounding to the storage type)
 };
 
 // KS: k-steps of 32 channels (taps x channel blocks), at most RW_KMAX
@@ -378,7 +379,18 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void polyrw_kernel(const RWA
                         const float v = acc[rb][c][i] + bv[rb];
                         f[i] = a.act == CTCONV_ACT_ELU ? elu_act<TR>(v) : v;
                     }
-                    if (o0 >= 0 && o0 + 3 < a.Lo) {
+                    if (a.outf32) {
+                        // fp32 output (a chunk of a stream, rounded later)
+                        float* frow = static_cast<float*>(a.y) + ((int64_t)n * a.C_out + co) * a.Lo;
+                        if (o0 >= 0 && o0 + 3 < a.Lo) {
+                            store16_unaligned(frow + o0, u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]),
+                                                               __float_as_uint(f[2]), __float_as_uint(f[3])});
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if (o0 + i >= 0 && o0 + i < a.Lo) frow[o0 + i] = f[i];
+                        }
+                    } else if (o0 >= 0 && o0 + 3 < a.Lo) {
                         *reinterpret_cast<u32x2_u*>(yrow + o0) =
                             u32x2{pack2<TR>(f[0], f[1]), pack2<TR>(f[2], f[3])};
                     } else {
@@ -532,9 +544,10 @@ bool polyrw_supported(const Problem& p) {
 }
 
 hipError_t launch_polyrw(const Problem& p, const void* x, const void* pw, const void* bias,
-                         void* y, hipStream_t s) {
+                         void* y, bool out_f32, hipStream_t s) {
     RWArgs a{};
     if (!plan_rw(p, &a)) return hipErrorInvalidValue;
+    a.outf32 = out_f32 ? 1 : 0;
     a.x = x;
     a.pw = pw;
     a.bias = bias;

@@ -7,9 +7,10 @@
 // and the k - s outputs from F*s on still await later frames (ExecuTorch PR
 // #25037: Phonon's StreamingConvTranspose1d holds that tail back between
 // 80 ms frames, and feeds the bias both to the conv and to the tail
-// bookkeeping).  Here the chunk's convolution is computed without bias, the
-// tail is kept as fp32 partial sums without bias, and the bias (and the
-// activation) is applied exactly once, when an output is emitted.
+// bookkeeping).  Here the chunk's convolution is computed without bias into
+// an fp32 workspace (no rounding), the tail is kept as fp32 partial sums
+// without bias, and the bias and the activation are applied, and the result
+// rounded to the storage type, exactly once, when an output is emitted.
 //
 // overlap: one chunk of L frames, z = convT(chunk) of length L*s + (k - s):
 //   y[o]        = act(z[o] + tail_in[o] + bias)      o <  L*s (tail_in[o] = 0 past k - s)
@@ -23,7 +24,7 @@ namespace ctconv {
 namespace {
 
 template <class TR>
-__global__ __launch_bounds__(256) void overlap_kernel(const typename TR::storage* __restrict__ z,
+__global__ __launch_bounds__(256) void overlap_kernel(const float* __restrict__ z,
                                                       const float* __restrict__ tail_in,
                                                       const typename TR::storage* __restrict__ bias,
                                                       typename TR::storage* __restrict__ y,
@@ -35,7 +36,7 @@ __global__ __launch_bounds__(256) void overlap_kernel(const typename TR::storage
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t row = i / Lz, o = i - row * Lz;
-        float v = TR::to_f32(z[i]);
+        float v = z[i];
         if (tail_in != nullptr && o < Tl) v += tail_in[row * Tl + o];
         if (o < Ly) {
             if (bias != nullptr) v += TR::to_f32(bias[row % C_out]);
@@ -71,12 +72,12 @@ int64_t grid_for(int64_t work) {
 }
 
 template <class TR>
-hipError_t overlap_t(const void* z, const float* tail_in, const void* bias, void* y,
+hipError_t overlap_t(const float* z, const float* tail_in, const void* bias, void* y,
                      float* tail_out, int64_t rows, int64_t C_out, int64_t Ly, int64_t Tl, int act,
                      hipStream_t s) {
     using S = typename TR::storage;
     overlap_kernel<TR><<<dim3((unsigned)grid_for(rows * (Ly + Tl))), dim3(256), 0, s>>>(
-        static_cast<const S*>(z), tail_in, static_cast<const S*>(bias), static_cast<S*>(y),
+        z, tail_in, static_cast<const S*>(bias), static_cast<S*>(y),
         tail_out, rows, C_out, Ly, Tl, act);
     return hipGetLastError();
 }
@@ -92,7 +93,7 @@ hipError_t flush_t(const float* tail_in, const void* bias, void* y, int64_t rows
 
 }  // namespace
 
-hipError_t launch_stream_overlap(const void* z, const float* tail_in, const void* bias, void* y,
+hipError_t launch_stream_overlap(const float* z, const float* tail_in, const void* bias, void* y,
                                  float* tail_out, int64_t rows, int64_t C_out, int64_t Ly,
                                  int64_t Tl, ctconv_dtype dt, int act, hipStream_t s) {
     if (rows * (Ly + Tl) <= 0) return hipSuccess;
