@@ -16,7 +16,8 @@
 // output depends only on its row oy and on ox mod sW: the outputs
 // ox = sW*ax + bx of one row and one column phase bx share the tap set, and
 // tap tx reads input column ax + c_tx with c_tx = (bx + pW - tx*dW) / sW.  A
-// workgroup takes 64 such outputs (consecutive ax) for 32 output channels.
+// workgroup takes 64 such outputs (consecutive ax) for 32 output channels,
+// for each column phase in turn.
 // Per 32-channel chunk of C_in and per valid tap row it stages in LDS, as
 // fp32, the x row segment all its taps read (zeros outside the input) and
 // the weights of its valid taps, then every lane accumulates 32 output
@@ -78,14 +79,21 @@ __global__ __launch_bounds__(256) void gather_staged_kernel(const GArgs a) {
     const int pos = wave * 16 + (lane & 15);  // output within the tile
     const int kq = lane >> 4;                 // quarter of the chunk's channels
 
-    for (int64_t tile = blockIdx.x; tile < a.tiles; tile += gridDim.x) {
-        __syncthreads();  // the previous tile's reads of tcs, xs and ws are done
-        // tile = (((n * n_cob + cob) * Ho + oy) * sW + bx) * n_axb + axb
+    // Tiles of consecutive workgroups of one XCD (dispatched round robin over
+    // the 8 XCDs) are consecutive, and a tile runs every column phase of its
+    // outputs itself: the sW interleaved phases of an output row segment are
+    // written by one workgroup close together in time, so its cache lines
+    // are completed in one L2 before they go to memory.
+    const int64_t wgid = (gridDim.x % 8u == 0)
+                             ? (int64_t)(blockIdx.x % 8u) * (gridDim.x / 8u) + blockIdx.x / 8u
+                             : (int64_t)blockIdx.x;
+    for (int64_t tile = wgid; tile < a.tiles; tile += gridDim.x)
+    for (int bx = 0; bx < a.sW; ++bx) {
+        __syncthreads();  // the previous step's reads of tcs, xs and ws are done
+        // tile = ((n * n_cob + cob) * Ho + oy) * n_axb + axb
         int64_t r = tile;
         const int axb = (int)(r % a.n_axb);
         r /= a.n_axb;
-        const int bx = (int)(r % a.sW);
-        r /= a.sW;
         const int oy = (int)(r % a.Ho);
         r /= a.Ho;
         const int cob = (int)(r % a.n_cob);
@@ -330,10 +338,11 @@ hipError_t launch_gather_t(const Problem& p, const void* x, const void* pw, cons
         const int64_t Aq = (p.Wo + p.sW - 1) / p.sW;
         a.n_axb = (int)((Aq + kGAx - 1) / kGAx);
         a.n_cob = (int)((p.C_out + kGCo - 1) / kGCo);
-        a.tiles = p.N * a.n_cob * p.Ho * p.sW * a.n_axb;
+        a.tiles = p.N * a.n_cob * p.Ho * a.n_axb;
         a.act = p.act;
         int64_t blocks = a.tiles;
         if (blocks > 256 * 64) blocks = 256 * 64;
+        if (blocks >= 64) blocks = blocks / 8 * 8;  // (the XCD-contiguous tile order)
         gather_staged_kernel<TR, OUTF><<<dim3((unsigned)blocks), dim3(256), 0, s>>>(a);
         return hipGetLastError();
     }
