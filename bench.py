@@ -64,6 +64,9 @@ def parse():
                     help="batch items of the workload in the oracle's timed sample")
     ap.add_argument("--cpu-frames", type=int, default=0,
                     help="leading input frames per item in the sample (0: all)")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="run the workload at this batch size instead of its own (one GPU's "
+                         "share of a batch split over several GPUs)")
     ap.add_argument("--stream-frames", type=int, default=0,
                     help="also time a streaming decode (N = 1) of the 1-D stack with this many "
                          "input frames per call (12 frames = 80 ms of 24 kHz audio for the "
@@ -289,6 +292,9 @@ def main():
     C.load()
     torch.cuda.set_device(0)
     wl = I.workload(args.workload)
+    if args.batch > 0:
+        import dataclasses
+        wl = dataclasses.replace(wl, N=args.batch)
     geo = layer_geometry(wl)
     tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[wl.dtype]
 
