@@ -147,7 +147,11 @@ extern "C" {
 int ctconv_abi_version(void) { return CTCONV_ABI_VERSION; }
 
 const char* ctconv_status_string(ctconv_status status) {
-    switch (status) {
+    // a C caller may pass any int: read it as one (a C++ enum object must not
+    // hold a value outside its enumerators)
+    int v;
+    memcpy(&v, &status, sizeof v);
+    switch (v) {
         case CTCONV_OK: return "ok";
         case CTCONV_ERR_NULL: return "a required pointer is NULL";
         case CTCONV_ERR_SHAPE: return "invalid or overflowing size";
