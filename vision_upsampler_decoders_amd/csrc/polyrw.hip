@@ -68,7 +68,7 @@ struct RWArgs {
     const void* pw;
     const void* bias;
     void* y;
-    int64_t Lo;         // output length
+    int Lo;             // output length
     int64_t n_tiles;    // N * tiles per image
     int L;              // input length
     int C_in, C_out, C_in_pad, ncb;  // ncb = C_in_pad / 32
@@ -82,12 +82,17 @@ struct RWArgs {
     uint32_t plane;     // bytes of one input channel (2 L)
     uint32_t img;       // bytes of one image (C_in * plane)
     uint32_t pw_bytes;
-    int act;
-    int outf32;         // 1: y is fp32 (no rounding to the storage type)
+    FastDiv fd_tpi;     // division by tpi (tile indices < 2^31)
 };
 
+// Epilogue modes (compile time, so that neither the activation nor the
+// output type costs a select per element): the storage type with no
+// activation, the storage type after ELU, fp32 with no activation (a chunk
+// of a stream, rounded later).
+enum RWEpi { RW_PLAIN = 0, RW_ELU = 1, RW_F32 = 2 };
+
 // KS: k-steps of 32 channels (taps x channel blocks), at most RW_KMAX
-template <class TR, bool XODD, int KS, int WAVES, int NP, int NBUF>
+template <class TR, bool XODD, int KS, int WAVES, int NP, int NBUF, int EPI>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void polyrw_kernel(const RWArgs a) {
     constexpr int THREADS = 64 * WAVES;
     constexpr int RW_ROWS = 32 * WAVES;            // rows of a workgroup
@@ -197,8 +202,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void polyrw_kernel(const RWA
     std::conditional_t<NBUF == 2, XBuf, char> bufB;
 
     auto tile_of = [&](int64_t tl, int& n, int& q0) __attribute__((always_inline)) {
-        n = (int)(tl / a.tpi);
-        q0 = (int)(tl - (int64_t)n * a.tpi) * RW_BQ;
+        const uint32_t t = (uint32_t)tl, nn = fdiv(t, a.fd_tpi);
+        n = (int)nn;
+        q0 = (int)(t - nn * (uint32_t)a.tpi) * RW_BQ;
     };
 
     // Global -> registers for tile tl (loads only; the values are consumed
@@ -361,36 +367,40 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void polyrw_kernel(const RWA
 
         int n, q0;
         tile_of(cur, n, q0);
-        {
-            // each lane writes its four consecutive outputs as one 8-byte run;
-            // a wave's four stores per row block cover 512 consecutive bytes
-            // of four output rows
+        // outputs s*q + j - p of this tile's positions q0 .. q0 + 63: when
+        // all of them lie inside the row no lane needs a bounds check
+        const int olo = a.s * q0 - a.p, ohi = a.s * (q0 + RW_BQ) - a.p;
+        const bool inside = olo >= 0 && ohi <= a.Lo;
+        // each lane writes its four consecutive outputs as one run; a wave's
+        // four stores per row block cover 512 (fp32: 1024) consecutive bytes
+        // of four output rows
 #pragma unroll
-            for (int rb = 0; rb < RW_RB; ++rb) {
-                const int co = co_e[rb];
-                if (co >= a.C_out) continue;
-                S* yrow = yg + ((int64_t)n * a.C_out + co) * a.Lo;
+        for (int rb = 0; rb < RW_RB; ++rb) {
+            const int co = co_e[rb];
+            if (co >= a.C_out) continue;
+            const int64_t row = ((int64_t)n * a.C_out + co) * a.Lo;
 #pragma unroll
-                for (int c = 0; c < RW_CB; ++c) {
-                    const int64_t o0 = (int64_t)a.s * (q0 + c * 16 + li) + j0_e[rb] - a.p;
-                    float f[4];
+            for (int c = 0; c < RW_CB; ++c) {
+                const int o0 = a.s * (q0 + c * 16 + li) + j0_e[rb] - a.p;
+                float f[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float v = acc[rb][c][i] + bv[rb];
-                        f[i] = a.act == CTCONV_ACT_ELU ? elu_act<TR>(v) : v;
+                for (int i = 0; i < 4; ++i) {
+                    const float v = acc[rb][c][i] + bv[rb];
+                    f[i] = EPI == RW_ELU ? elu_act<TR>(v) : v;
+                }
+                if constexpr (EPI == RW_F32) {
+                    float* frow = static_cast<float*>(a.y) + row;
+                    if (inside || (o0 >= 0 && o0 + 3 < a.Lo)) {
+                        store16_unaligned(frow + o0, u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]),
+                                                           __float_as_uint(f[2]), __float_as_uint(f[3])});
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (o0 + i >= 0 && o0 + i < a.Lo) frow[o0 + i] = f[i];
                     }
-                    if (a.outf32) {
-                        // fp32 output (a chunk of a stream, rounded later)
-                        float* frow = static_cast<float*>(a.y) + ((int64_t)n * a.C_out + co) * a.Lo;
-                        if (o0 >= 0 && o0 + 3 < a.Lo) {
-                            store16_unaligned(frow + o0, u32x4{__float_as_uint(f[0]), __float_as_uint(f[1]),
-                                                               __float_as_uint(f[2]), __float_as_uint(f[3])});
-                        } else {
-#pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                if (o0 + i >= 0 && o0 + i < a.Lo) frow[o0 + i] = f[i];
-                        }
-                    } else if (o0 >= 0 && o0 + 3 < a.Lo) {
+                } else {
+                    S* yrow = yg + row;
+                    if (inside || (o0 >= 0 && o0 + 3 < a.Lo)) {
                         *reinterpret_cast<u32x2_u*>(yrow + o0) =
                             u32x2{pack2<TR>(f[0], f[1]), pack2<TR>(f[2], f[3])};
                     } else {
@@ -462,23 +472,33 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void polyrw_kernel(const RWA
 
 using RWFn = void (*)(const RWArgs);
 
-template <class TR, int KS>
+template <class TR, int KS, int EPI>
 RWFn pick_ks(bool xodd) {
-    return xodd ? &polyrw_kernel<TR, true, KS, RW_WAVES, RW_NP, RW_NBUF>
-                : &polyrw_kernel<TR, false, KS, RW_WAVES, RW_NP, RW_NBUF>;
+    return xodd ? &polyrw_kernel<TR, true, KS, RW_WAVES, RW_NP, RW_NBUF, EPI>
+                : &polyrw_kernel<TR, false, KS, RW_WAVES, RW_NP, RW_NBUF, EPI>;
+}
+
+template <class TR, int EPI>
+RWFn pick_e(bool xodd, int ks) {
+    switch (ks) {
+        case 1: return pick_ks<TR, 1, EPI>(xodd);
+        case 2: return pick_ks<TR, 2, EPI>(xodd);
+        case 3: return pick_ks<TR, 3, EPI>(xodd);
+        case 4: return pick_ks<TR, 4, EPI>(xodd);
+        case 5: return pick_ks<TR, 5, EPI>(xodd);
+        case 6: return pick_ks<TR, 6, EPI>(xodd);
+        case 7: return pick_ks<TR, 7, EPI>(xodd);
+        case 8: return pick_ks<TR, 8, EPI>(xodd);
+    }
+    return nullptr;
 }
 
 template <class TR>
-RWFn pick(bool xodd, int ks) {
-    switch (ks) {
-        case 1: return pick_ks<TR, 1>(xodd);
-        case 2: return pick_ks<TR, 2>(xodd);
-        case 3: return pick_ks<TR, 3>(xodd);
-        case 4: return pick_ks<TR, 4>(xodd);
-        case 5: return pick_ks<TR, 5>(xodd);
-        case 6: return pick_ks<TR, 6>(xodd);
-        case 7: return pick_ks<TR, 7>(xodd);
-        case 8: return pick_ks<TR, 8>(xodd);
+RWFn pick(bool xodd, int ks, int epi) {
+    switch (epi) {
+        case RW_PLAIN: return pick_e<TR, RW_PLAIN>(xodd, ks);
+        case RW_ELU: return pick_e<TR, RW_ELU>(xodd, ks);
+        case RW_F32: return pick_e<TR, RW_F32>(xodd, ks);
     }
     return nullptr;
 }
@@ -496,10 +516,12 @@ bool plan_rw(const Problem& p, RWArgs* a) {
     const int64_t pw_bytes = p.sW * p.C_out * p.mW * p.C_in_pad * 2;
     if (pw_bytes >= 0x7FFFFFF0LL) return false;
     const int64_t Q = (p.Wo - 1 + p.pW) / p.sW + 1;  // q positions reaching an output
-    if (Q + RW_BQ > 0x3FFFFFFFLL || p.Wo > 0x3FFFFFFFFFFFLL) return false;
+    // int positions and output indices (s * (q + 64) stays below 2^31)
+    if (Q + RW_BQ > 0x3FFFFFFFLL || p.Wo > 0x3FFFFFFFLL || (Q + RW_BQ) * p.sW > 0x7FFFFFFFLL)
+        return false;
     if (p.C_out * p.sW > 0x3FFFFFFFLL) return false;
     const int64_t tpi = (Q + RW_BQ - 1) / RW_BQ;
-    a->Lo = p.Wo;
+    a->Lo = (int)p.Wo;
     a->n_tiles = p.N * tpi;
     a->L = (int)p.W;
     a->C_in = (int)p.C_in;
@@ -511,6 +533,8 @@ bool plan_rw(const Problem& p, RWArgs* a) {
     a->T = (int)p.mW;
     a->KS = a->T * a->ncb;
     a->tpi = (int)tpi;
+    a->fd_tpi = make_fastdiv((uint32_t)tpi);
+    if (a->n_tiles > 0x7FFFFFFFLL) return false;  // 32-bit tile indices
     a->rg = (int)((p.C_out * p.sW + RW_ROWS - 1) / RW_ROWS);
     // (8 / WAVES) workgroups per CU; at least four tiles per workgroup
     int64_t per = 256 * (8 / RW_WAVES) / a->rg;
@@ -528,7 +552,6 @@ bool plan_rw(const Problem& p, RWArgs* a) {
     a->plane = (uint32_t)(p.W * 2);
     a->img = (uint32_t)img;
     a->pw_bytes = (uint32_t)pw_bytes;
-    a->act = p.act;
     // (with m * C_in_pad <= 256 the window's load items fit one per thread)
     // the two x stages within RW_LDS_MAX bytes of dynamic LDS
     if (2 * (int64_t)a->stage * 2 > RW_LDS_MAX) return false;
@@ -547,13 +570,15 @@ hipError_t launch_polyrw(const Problem& p, const void* x, const void* pw, const 
                          void* y, bool out_f32, hipStream_t s) {
     RWArgs a{};
     if (!plan_rw(p, &a)) return hipErrorInvalidValue;
-    a.outf32 = out_f32 ? 1 : 0;
+    // the fp32 output of a stream chunk takes no activation
+    if (out_f32 && p.act != CTCONV_ACT_NONE) return hipErrorInvalidValue;
+    const int epi = out_f32 ? RW_F32 : (p.act == CTCONV_ACT_ELU ? RW_ELU : RW_PLAIN);
     a.x = x;
     a.pw = pw;
     a.bias = bias;
     a.y = y;
     const bool xodd = (p.W % 2) == 1;
-    RWFn fn = p.dtype == CTCONV_BF16 ? pick<TBF16>(xodd, a.KS) : pick<TF16>(xodd, a.KS);
+    RWFn fn = p.dtype == CTCONV_BF16 ? pick<TBF16>(xodd, a.KS, epi) : pick<TF16>(xodd, a.KS, epi);
     if (fn == nullptr) return hipErrorInvalidValue;
     const size_t lds = (size_t)(2 * a.stage) * 2;  // at most RW_LDS_MAX
     hipLaunchKernelGGL(fn, dim3((unsigned)(a.rg * a.wg_per_rg)), dim3(RW_THREADS), lds, s, a);
