@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="vocoder_stack")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock-probe", action="store_true",
+                    help="skip the sustained-clock probe (about 2 ms of GPU time after the timing)")
     ap.add_argument("--cold-reps", type=int, default=20,
                     help="steps timed after a 512 MiB cache flush (at most --steps)")
     ap.add_argument("--separate-elu", action="store_true",
@@ -489,6 +491,18 @@ def main():
     roof["cold"] = {"achieved": round(ach_c, 2 if roof["bound"] != "hbm" else 1),
                     "frac": round(ach_c / roof["peak"], 4), "median_launch_us": round(t_c * 1e6, 2),
                     "reps": cold_reps}
+    # The published peaks hold at 2400 MHz.  The clock the chip keeps under
+    # full matrix-core load (ctconv_clock_probe, after the timed region)
+    # scales the compute peaks; HBM's peak does not depend on it.
+    if not args.no_clock_probe:
+        mhz, probe_tf = C.sustained_clock(iters=4096)
+        roof["clock"] = {"sustained_mhz": round(mhz, 1), "spec_mhz": 2400.0,
+                         "probe_bf16_tflops": round(probe_tf, 1),
+                         "how": "s_memtime / s_memrealtime (100 MHz) over a probe keeping every "
+                                "matrix core busy"}
+        if roof["bound"] != "hbm":
+            roof["frac_at_sustained_clock"] = round(
+                roof["achieved"] / (roof["peak"] * mhz / 2400.0), 4)
 
 
     res = {

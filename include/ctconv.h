@@ -408,6 +408,29 @@ ctconv_status ctconv_depthwise_query_kernel(int64_t N, int64_t C_in, int64_t C_o
                                             const int64_t* dilation, ctconv_dtype dtype,
                                             ctconv_dw_kernel* which);
 
+/*
+ * Sustained shader clock (a measurement aid for roofline fractions, not part
+ * of the transposed convolution; callers: benchmarks).  The MI355X peaks are
+ * quoted at 2.4 GHz; under load the chip may hold a lower clock.  The probe
+ * keeps every matrix core issuing bf16 MFMAs (16 independent accumulation
+ * chains per wave, two 8-wave workgroups per compute unit, `iters` rounds of
+ * 16 MFMAs per wave) and reads, per workgroup, the shader-clock cycle
+ * counter (s_memtime) and the 100 MHz real-time counter (s_memrealtime) at
+ * its start and end.
+ *   workspace        device buffer, 8-byte aligned, of at least
+ *                    ctconv_clock_probe_bytes() bytes (overwritten)
+ *   workspace_bytes  its size
+ *   iters            1 .. 2^24 (4096 runs about 2 ms)
+ *   mhz              out: shader cycles / real time over all workgroups, MHz
+ *   tflops           out (may be NULL): the probe's bf16 MFMA rate, TFLOP/s
+ * Errors: CTCONV_ERR_NULL (workspace or mhz NULL), CTCONV_ERR_PARAM (iters),
+ * CTCONV_ERR_WORKSPACE (too small), CTCONV_ERR_ALIGN, CTCONV_ERR_HIP.
+ * Synchronous: returns after the probe kernel has finished on `stream`.
+ */
+size_t ctconv_clock_probe_bytes(void);
+ctconv_status ctconv_clock_probe(void* workspace, size_t workspace_bytes, int iters, double* mhz,
+                                 double* tflops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

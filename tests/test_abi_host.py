@@ -405,3 +405,14 @@ def test_noalloc_rejects_beyond_scratch_before_any_device_call(lib):
     st = lib.ctconv_forward_noalloc(0x1000, 0x2000, None, 0x3000, 1, 0, 2, nd, arr((1024,)),
                                     arr(4096), arr(2048), arr(0), arr(0), arr(1), 0, 0, None)
     assert st == 2
+
+
+def test_clock_probe_validates_before_any_device_call(lib):
+    mhz = ctypes.c_double()
+    # NULL workspace / NULL result, then an iteration count out of range
+    assert lib.ctconv_clock_probe(None, 1 << 20, 4096, ctypes.byref(mhz), None, None) == 1
+    assert lib.ctconv_clock_probe(ctypes.c_void_p(4096), 1 << 20, 4096, None, None, None) == 1
+    assert lib.ctconv_clock_probe(ctypes.c_void_p(4096), 1 << 20, 0, ctypes.byref(mhz), None,
+                                  None) == 3
+    assert lib.ctconv_clock_probe(ctypes.c_void_p(4096), 1 << 20, (1 << 24) + 1,
+                                  ctypes.byref(mhz), None, None) == 3

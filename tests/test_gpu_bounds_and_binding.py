@@ -137,3 +137,23 @@ def test_explicit_stream_waits_for_current(cc):
         side.synchronize()
         torch.cuda.synchronize()
         assert torch.equal(y, ref)
+
+
+def test_clock_probe(cc):
+    """The sustained-clock probe returns a clock in the chip's range and an
+    MFMA rate below the published bf16 peak; a short workspace is refused."""
+    import ctypes
+
+    import torch
+
+    say("clock probe")
+    mhz, tflops = cc.sustained_clock(iters=2048)
+    assert 800.0 < mhz < 2600.0, mhz
+    assert 100.0 < tflops < 2516.6 * 1.05, tflops
+    nb = cc.ctconv_clock_probe_bytes()
+    assert nb > 0
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    out = ctypes.c_double()
+    st = cc.load().ctconv_clock_probe(ctypes.c_void_p(ws.data_ptr()), nb - 8, 16,
+                                      ctypes.byref(out), None, None)
+    assert st == 7

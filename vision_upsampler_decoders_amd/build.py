@@ -31,7 +31,7 @@ FLAGS = [
 ]
 
 SOURCES = ["ctconv_api.hip", "prepack.hip", "gather.hip", "pointwise.hip", "stream.hip",
-           "depthwise.hip", "polyphase.hip", "polyrw.hip", "noalloc.hip"]
+           "depthwise.hip", "polyphase.hip", "polyrw.hip", "noalloc.hip", "clock.hip"]
 
 
 def _compile(src: str) -> str:

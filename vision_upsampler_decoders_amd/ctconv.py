@@ -28,7 +28,7 @@ EXPORTED = (
     "ctconv_stream_flush", "ctconv_istft_normalize", "ctconv_depthwise_forward",
     "ctconv_depthwise_forward_kernel", "ctconv_depthwise_query_kernel",
     "ctconv_workspace_bytes", "ctconv_forward_ws", "ctconv_forward_noalloc",
-    "ctconv_scratch_bytes",
+    "ctconv_scratch_bytes", "ctconv_clock_probe_bytes", "ctconv_clock_probe",
 )
 
 DW_AUTO, DW_ROW, DW_ELEMENT = 0, 1, 2
@@ -87,6 +87,11 @@ def load(path: str = LIB_PATH):
     lib.ctconv_forward_noalloc.restype = c_int
     lib.ctconv_scratch_bytes.argtypes = []
     lib.ctconv_scratch_bytes.restype = ctypes.c_size_t
+    lib.ctconv_clock_probe_bytes.argtypes = []
+    lib.ctconv_clock_probe_bytes.restype = ctypes.c_size_t
+    lib.ctconv_clock_probe.argtypes = [c_vp, ctypes.c_size_t, c_int, ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_double), c_vp]
+    lib.ctconv_clock_probe.restype = c_int
     lib.ctconv_depthwise_forward.argtypes = fwd + [c_int, c_vp]
     lib.ctconv_depthwise_forward.restype = c_int
     lib.ctconv_depthwise_forward_kernel.argtypes = fwd + [c_int, c_int, c_vp]
@@ -251,6 +256,19 @@ def ctconv_scratch_bytes() -> int:
     return int(load().ctconv_scratch_bytes())
 
 
+def ctconv_clock_probe_bytes() -> int:
+    return int(load().ctconv_clock_probe_bytes())
+
+
+def ctconv_clock_probe(ws_ptr: int, ws_bytes: int, iters: int, stream: int):
+    """(sustained shader clock in MHz, the probe's bf16 MFMA TFLOP/s); synchronous."""
+    mhz, tf = ctypes.c_double(), ctypes.c_double()
+    st = load().ctconv_clock_probe(ws_ptr, ws_bytes, iters, ctypes.byref(mhz), ctypes.byref(tf),
+                                   stream)
+    _check("ctconv_clock_probe", st)
+    return mhz.value, tf.value
+
+
 def ctconv_query_route(N: int, C_in: int, C_out: int, in_spatial, kernel, stride, padding=0,
                        output_padding=0, dilation=1, dtype: int = CTCONV_F32) -> int:
     ndim = len(in_spatial)
@@ -405,6 +423,15 @@ def _check_tensor(name, t, dtype, device, shape=None, numel=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if numel is not None and t.numel() != numel:
         raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+
+
+def sustained_clock(iters: int = 4096, device=None, stream=None):
+    """(MHz, TFLOP/s) of ctconv_clock_probe on `device` (a workspace is allocated here)."""
+    torch = _torch()
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    nb = ctconv_clock_probe_bytes()
+    ws = torch.empty(max(nb, 8), dtype=torch.uint8, device=dev)
+    return ctconv_clock_probe(ws.data_ptr(), ws.numel(), iters, _stream(stream))
 
 
 def prepack(w, stride, stream=None):
