@@ -399,7 +399,8 @@ ctconv_status ctconv_stream_step(const void* x, const void* packed_w, const void
     // z = convT(chunk) with padding 0 and no bias, in fp32, into the
     // workspace: fp32 inputs through the ordinary forward; 16-bit inputs
     // through the register-weight streaming kernel where it applies, else the
-    // gather kernel, both writing their fp32 accumulators unrounded
+    // tiled kernel, else the gather kernel, each writing its fp32
+    // accumulators unrounded
     const int64_t one = 1, zero = 0;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     if (dtype == CTCONV_F32) {
@@ -413,9 +414,11 @@ ctconv_status ctconv_stream_step(const void* x, const void* packed_w, const void
                            dtype, &p);
         if (st != CTCONV_OK) return st;
         p.act = CTCONV_ACT_NONE;
-        const hipError_t e = polyrw_supported(p)
-                                 ? launch_polyrw(p, x, packed_w, nullptr, workspace, true, hs)
-                                 : launch_gather(p, x, packed_w, nullptr, workspace, true, hs);
+        float* z = static_cast<float*>(workspace);
+        const hipError_t e =
+            polyrw_supported(p)             ? launch_polyrw(p, x, packed_w, nullptr, z, true, hs)
+            : polyphase_f32out_supported(p) ? launch_polyphase_f32out(p, x, packed_w, z, hs)
+                                            : launch_gather(p, x, packed_w, nullptr, z, true, hs);
         if (e != hipSuccess) return to_status(e);
     }
     return to_status(launch_stream_overlap(static_cast<const float*>(workspace), tail_in, bias, y,

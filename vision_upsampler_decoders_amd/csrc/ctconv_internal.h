@@ -161,6 +161,9 @@ struct PolyArgs {
     int xcd_remap;         // 1: gridDim.x is a multiple of 8, remap for L2 locality
     uint32_t pw_bytes;     // size of the packed weight (below 2^32)
     int act;               // ctconv_activation of the epilogue
+    int outf32;            // 1: y is fp32, written straight from the accumulators (1-D
+                           // shapes without padding shift classes, reduction or split:
+                           // the chunks of a 16-bit stream)
     // Dilation (per dimension): the kernel runs the problem reduced by
     // g = gcd(s, d) (stride s/g), whose output u' sits at o0 + g*u' of the
     // real output; the other outputs are bias only (pre-filled).  Identity
@@ -230,5 +233,12 @@ hipError_t launch_polyrw(const Problem& p, const void* x, const void* pw, const 
                          void* y, bool out_f32, hipStream_t s);
 hipError_t launch_polyphase(const Problem& p, const void* x, const void* pw, const void* bias,
                             void* y, void* ws, size_t ws_bytes, hipStream_t s);
+// The tiled kernel with fp32 outputs and no bias or activation, for 16-bit
+// 1-D shapes (the conv part of a stream step); false / hipErrorInvalidValue
+// where its plan would shift padding by phase class, reduce a dilation or
+// split the reduction.
+bool polyphase_f32out_supported(const Problem& p);
+hipError_t launch_polyphase_f32out(const Problem& p, const void* x, const void* pw, float* y,
+                                   hipStream_t s);
 
 }  // namespace ctconv

@@ -45,6 +45,7 @@ constexpr int kGAx = 64;     // outputs (consecutive ax) per workgroup
 constexpr int kGCo = 32;     // output channels per workgroup (in registers)
 constexpr int kGKc = 32;     // input channels per staged chunk
 constexpr int kGTx = 8;      // valid column taps per row, at most
+constexpr int kGMinTiles = 64;   // tiles below which the per-lane kernel runs instead
 constexpr int kGXw = 128;    // staged x columns: kGAx + the taps' reach
 constexpr int kGQ = 4;       // lanes sharing one output (quarters of a chunk)
 
@@ -311,7 +312,13 @@ template <class TR, bool OUTF>
 hipError_t launch_gather_t(const Problem& p, const void* x, const void* pw, const void* bias,
                            void* y, hipStream_t s) {
     using S = typename TR::storage;
-    if (gather_staged_ok(p)) {
+    // The staged kernel keeps a workgroup on one tile through every phase,
+    // tap and channel chunk: with very few tiles (small problems, such as
+    // the frames of a stream: eight tiles per layer) that chain runs on a
+    // few workgroups, and the per-lane kernel's spread over many lanes wins.
+    const int64_t n_tiles = p.N * ((p.C_out + kGCo - 1) / kGCo) * p.Ho *
+                            (((p.Wo + p.sW - 1) / p.sW + kGAx - 1) / kGAx);
+    if (gather_staged_ok(p) && n_tiles >= kGMinTiles) {
         GArgs a{};
         a.x = x;
         a.pw = pw;

@@ -724,6 +724,32 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     // done reading them
     __syncthreads();
 
+    // ---- fp32 outputs straight from the accumulators (1-D, no padding
+    // shift classes or reduction: the chunks of a 16-bit stream, whose
+    // outputs are few): one 4-byte store per element, rounded nowhere
+    if (a.outf32) {
+        if constexpr (C::TAY == 1) {
+            float* __restrict__ yf = static_cast<float*>(a.y);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                int pb, co_l;
+                col_map(bcol + cb * 16, pb, co_l);
+                const int b = b0 + pb, co = co0 + co_l;
+                if (pb >= a.PT || b >= a.P || co_l >= a.TCO || co >= a.C_out) continue;
+                float* yrow = yf + (n * a.C_out + co) * a.WoR;
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int64_t ax = ax0 + (wm * RB + rb) * 16 + lg * 4 + i;
+                        const int64_t ox = ax * a.sx + b - a.oxs;
+                        if (ox >= 0 && ox < a.WoR) yrow[ox] = acc[rb][cb][i] + bvs[cb];
+                    }
+            }
+        }
+        return;
+    }
+
     // ---- epilogue: bias, round, stage in output order, store ---------------
     const int R = a.phase_subset ? TAX : C::TAY * a.sy;
     const int SS = a.phase_subset ? a.PT : TAX * a.sx;
@@ -1475,6 +1501,38 @@ size_t polyphase_workspace_bytes(const Problem& p) {
     int sp = 1;
     if (!plan(p, &a, &in, &sp, true) || sp <= 1) return 0;
     return (size_t)(sp - 1) * (size_t)a.ws_slab * sizeof(float);
+}
+
+namespace {
+
+bool plan_f32out(const Problem& p, PolyArgs* a, Inst* in) {
+    if (p.ndim != 1 || p.dtype == CTCONV_F32 || p.act != CTCONV_ACT_NONE) return false;
+    int splits = 1;
+    if (!plan(p, a, in, &splits, false)) return false;
+    return in->TAY == 1 && a->cmode == 0 && a->gx == 1 && a->gy == 1 && a->partial == 0 &&
+           splits == 1;
+}
+
+}  // namespace
+
+bool polyphase_f32out_supported(const Problem& p) {
+    PolyArgs a{};
+    Inst in{};
+    return plan_f32out(p, &a, &in);
+}
+
+hipError_t launch_polyphase_f32out(const Problem& p, const void* x, const void* pw, float* y,
+                                   hipStream_t s) {
+    PolyArgs a{};
+    Inst in{};
+    if (!plan_f32out(p, &a, &in)) return hipErrorInvalidValue;
+    a.x = x;
+    a.pw = pw;
+    a.bias = nullptr;
+    a.y = y;
+    a.outf32 = 1;
+    hipLaunchKernelGGL(in.fn, dim3((unsigned)a.n_tiles, 1u), dim3(in.threads), 0, s, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_polyphase(const Problem& p, const void* x, const void* pw, const void* bias,
