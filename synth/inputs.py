@@ -185,10 +185,11 @@ WORKLOADS: Dict[str, Workload] = {
         [_L(128, 64, 3, 2, 1, op=1, d=2, ndim=2)],
         ("uniform", -1.0, 1.0), "uniform",
         note="ConvTranspose2d fp32 128->64 3x3 s2 p1 op1 dilation 2, 96x96, N=4"),
-    # Shapes only the gather kernel takes: stride 3 in 2-D (nine phases, more
-    # than a 2-D column tile holds) with k not a multiple of s, and a 1-D
-    # kernel of eight taps per phase (more than any compiled polyphase
-    # instance), both fp32 in the family of the 3x3 stride-2 shapes above.
+    # Stride 3 in 2-D (nine phases, more than a 2-D column tile holds: the
+    # polyphase kernel's column tiles take subsets of them) with k not a
+    # multiple of s, and a shape only the gather kernel takes: a 1-D kernel
+    # of eight taps per phase (more than any compiled polyphase instance),
+    # both fp32 in the family of the 3x3 stride-2 shapes above.
     "gather2d_s3": Workload(
         8, "gather2d_s3", "f32", 4, (64, 64),
         [_L(128, 64, 5, 3, 1, op=1, ndim=2)],

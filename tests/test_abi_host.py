@@ -156,7 +156,7 @@ def test_forward_with_N_zero_enqueues_nothing(lib):
 
 @pytest.mark.parametrize("name,route", [
     ("upsampler1d_small", 1), ("vocoder_stack", 1), ("istft", 1), ("upsampler2d", 1),
-    ("gather2d", 1), ("gather2d_dil2", 1),
+    ("gather2d", 1), ("gather2d_dil2", 1), ("gather2d_s3", 1), ("gather1d_m8", 2),
 ])
 def test_routes_of_workloads(lib, name, route):
     from synth import inputs as I
@@ -196,7 +196,9 @@ def test_route_rule(lib, k, s, p, op, d, route):
 @pytest.mark.parametrize("k,s,p,op,d,route", [
     ((3, 3), (2, 2), (1, 1), (1, 1), (2, 2), 1),   # reduced: stride 1, 3 x 3 taps
     ((3, 3), (4, 4), (1, 1), (0, 0), (2, 2), 1),   # reduced: stride 2, 2 x 2 taps
-    ((3, 3), (3, 3), (1, 1), (0, 0), (2, 2), 2),   # 9 phases: more than a 2-D tile holds
+    ((3, 3), (3, 3), (1, 1), (0, 0), (2, 2), 1),   # 9 phases: tiles hold subsets of them
+    ((5, 5), (3, 3), (1, 1), (1, 1), (1, 1), 1),   # 9 phases, 2 x 2 taps
+    ((4, 4), (4, 4), (0, 0), (0, 0), (1, 1), 1),   # 16 phases, 1 x 1 tap
     ((3, 2), (3, 1), (1, 0), (2, 0), (2, 1), 1),   # y expanded: 5 taps at stride 3, 2 x 2
     ((3, 3), (2, 2), (1, 1), (0, 0), (3, 3), 2),   # expanded: 7 taps at stride 2, 4 x 4
     ((4, 2), (2, 2), (1, 2), (0, 1), (1, 3), 1),   # x expanded to 4 taps: 2 x 2
@@ -206,7 +208,7 @@ def test_route_rule(lib, k, s, p, op, d, route):
 def test_route_rule_2d_dilation(lib, k, s, p, op, d, route):
     # 2-D: per dimension reduction by gcd(s, d) and expansion of the rest of
     # the dilation; the compiled 2-D tap counts are 1 or 2 per dimension, or
-    # 3 x 3
+    # 3 x 3; any number of phases (column tiles take subsets of them)
     assert C.ctconv_query_route(2, 16, 16, (20, 22), k, s, p, op, d, 0) == route
 
 

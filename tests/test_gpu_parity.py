@@ -132,6 +132,11 @@ FULL_CASES = [
     ("len2_f32", "f32", 3, 40, 16, (2,), (8,), (4,), (2,), (0,), (1,), True),
     ("len4_bf16", "bf16", 3, 40, 24, (4,), (8,), (4,), (3,), (0,), (1,), True),
     ("w4_2d_bf16", "bf16", 2, 32, 16, (5, 4), (4, 4), (2, 2), (1, 1), (0, 0), (1, 1), True),
+    # 2-D with more phases than a column tile holds (tiles of phase subsets)
+    ("s3_2d_bf16", "bf16", 2, 48, 40, (13, 17), (5, 5), (3, 3), (1, 1), (1, 1), (1, 1), True),
+    ("s3_2d_f32_k3", "f32", 1, 40, 64, (21, 10), (3, 3), (3, 3), (0, 1), (2, 0), (1, 1), False),
+    ("s4_2d_f16", "f16", 2, 36, 24, (9, 11), (4, 4), (4, 4), (0, 0), (0, 0), (1, 1), True),
+    ("s4x3_2d_f32", "f32", 1, 24, 96, (7, 15), (8, 6), (4, 3), (2, 1), (0, 1), (1, 1), True),
     # odd input rows (2-byte-offset row pieces): odd length with ragged
     # channels, and a 2-D plane of odd size (odd channels 2 bytes off)
     ("odd_len_bf16", "bf16", 2, 40, 24, (301,), (8,), (4,), (2,), (0,), (1,), True),

@@ -751,7 +751,9 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     }
 
     // ---- epilogue: bias, round, stage in output order, store ---------------
-    const int R = a.phase_subset ? TAX : C::TAY * a.sy;
+    // staged rows per output channel: the tile's positions (phase subsets,
+    // whose phases go to the columns) or its output rows
+    const int R = a.phase_subset ? C::TAY * TAX : C::TAY * a.sy;
     const int SS = a.phase_subset ? a.PT : TAX * a.sx;
     // output-channel stride padded by 16 bytes: lanes of one MFMA column block
     // hold consecutive output channels, so an unpadded power-of-two stride
@@ -937,7 +939,7 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                         const int ayl = tr / TAX, axl = tr % TAX;
                         int rr, ss;
                         if (a.phase_subset) {
-                            rr = axl;
+                            rr = tr;  // = axl in 1-D
                             ss = pb;
                         } else {
                             rr = ayl * a.sy + by;
@@ -1007,6 +1009,27 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                     for (int q = s0 < lo ? lo : s0; q < qe; ++q) yg[gb[u] + q] = smem[sof[u] + q];
                 }
             }
+        }
+        return;
+    }
+    if (C::TAY > 1 && a.phase_subset) {
+        // 2-D phase subsets: the staged row of a position holds its phases
+        // b0 .. b0 + PT - 1, which lie in different output rows: element
+        // stores, each thread taking consecutive staged elements
+        const int64_t Hc = a.Ho - a.oys, Wc = a.Wo - a.oxs;
+        const int total = nrows * SS;
+        for (int idx = tid; idx < total; idx += C::NT) {
+            const int row = (int)fdiv((uint32_t)idx, a.fd_pt), e = idx - row * SS;
+            const int b = b0 + e;
+            const int co_l = (int)fdiv((uint32_t)row, a.fd_R), rr = row - co_l * R;
+            const int co = co0 + co_l;
+            if (b >= a.P || co >= a.C_out) continue;
+            const int by = (int)fdiv((uint32_t)b, a.fd_sx), bx = b - by * a.sx;
+            const int64_t oy = (int64_t)(ay0 + rr / TAX) * a.sy + by - a.oys;
+            const int64_t ox = (int64_t)(ax0 + rr % TAX) * a.sx + bx - a.oxs;
+            if (oy < 0 || oy >= Hc || ox < 0 || ox >= Wc) continue;
+            yg[((n * a.C_out + co) * a.HoR + (a.o0y + a.gy * oy)) * a.WoR + a.o0x + a.gx * ox] =
+                smem[co_l * CSTR + rr * SS + e];
         }
         return;
     }
@@ -1193,12 +1216,28 @@ bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allo
             const int64_t cpad = (p.C_out + 15) / 16 * 16;
             if (TCO > cpad) TCO = cpad;
         }
-    } else {
-        if (p.ndim != 1) return false;
+    } else if (p.ndim == 1) {
         subset = 1;
         TCO = tco_min;
         PT = BN / TCO;
-        if (!narrow) PT = PT / 1;  // 16-channel blocks, one phase each
+    } else {
+        // 2-D with more phases than a column tile holds (s = 3: 9, s = 4:
+        // 16): tiles of PT whole phases x TCO channels, TCO (a multiple of
+        // 16 dividing BN) chosen for the fewest column tiles
+        if (narrow) return false;
+        const int64_t cpad = (p.C_out + 15) / 16 * 16;
+        int64_t best = -1;
+        for (int64_t t = 16; t <= BN && t <= cpad; t += 16) {
+            if (BN % t != 0) continue;
+            const int64_t cost = ((p.C_out + t - 1) / t) * ((P + BN / t - 1) / (BN / t));
+            if (best < 0 || cost < best) {
+                best = cost;
+                TCO = t;
+            }
+        }
+        if (best < 0) return false;
+        subset = 1;
+        PT = BN / TCO;
     }
     if (TCO < 1 || PT < 1) return false;
     // class mode reads A fragments per 16-column block: one phase per block;
@@ -1324,7 +1363,7 @@ bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allo
     a->fd_tco = make_fastdiv((uint32_t)TCO);
     a->fd_sx = make_fastdiv((uint32_t)p.sW);
     a->fd_sy = make_fastdiv((uint32_t)p.sH);
-    a->fd_R = make_fastdiv((uint32_t)(subset ? in.TAX : in.TAY * p.sH));
+    a->fd_R = make_fastdiv((uint32_t)(subset ? in.TAY * in.TAX : in.TAY * p.sH));
     {
         // staged-row chunks of 16 bytes (flattened output stores)
         const int64_t vec = p.dtype == CTCONV_F32 ? 4 : 8;
