@@ -134,10 +134,11 @@ def test_forward_validation_before_launch(lib):
     assert _fwd(lib, x=0x1001) == 5
     assert _fwd(lib, y=0x3008) == 5
     assert _fwd(lib, b=0x4004) == 5
-    # polyphase forced on a shape outside the polyphase form
-    assert _fwd(lib, d=3, k=5, s=2, route=1) == 3    # 7 expanded taps per phase: no instance
-    assert _fwd(lib, d=2, k=9, s=2, route=1) == 3    # reduced problem with 9 taps
-    assert _fwd(lib, k=20, s=4, p=2, route=1) == 3   # 5 taps per phase
+    # polyphase forced on a shape outside the polyphase form (16-bit: fp32
+    # shapes with more taps per phase than an instance run as tap groups)
+    assert _fwd(lib, d=3, k=5, s=2, dt=1, route=1) == 3   # 7 expanded taps per phase
+    assert _fwd(lib, d=2, k=9, s=2, route=1) == 3          # reduced problem with 9 taps
+    assert _fwd(lib, k=20, s=4, p=2, dt=1, route=1) == 3   # 5 taps per phase
     assert _fwd(lib, sp=(3,), dt=1, route=1) == 3     # rows shorter than 8 bytes
     # fused activation: an unknown activation is rejected
     nd = 1
@@ -156,7 +157,7 @@ def test_forward_with_N_zero_enqueues_nothing(lib):
 
 @pytest.mark.parametrize("name,route", [
     ("upsampler1d_small", 1), ("vocoder_stack", 1), ("istft", 1), ("upsampler2d", 1),
-    ("gather2d", 1), ("gather2d_dil2", 1), ("gather2d_s3", 1), ("gather1d_m8", 2),
+    ("gather2d", 1), ("gather2d_dil2", 1), ("gather2d_s3", 1), ("gather1d_m8", 1),
 ])
 def test_routes_of_workloads(lib, name, route):
     from synth import inputs as I
@@ -200,7 +201,7 @@ def test_route_rule(lib, k, s, p, op, d, route):
     ((5, 5), (3, 3), (1, 1), (1, 1), (1, 1), 1),   # 9 phases, 2 x 2 taps
     ((4, 4), (4, 4), (0, 0), (0, 0), (1, 1), 1),   # 16 phases, 1 x 1 tap
     ((3, 2), (3, 1), (1, 0), (2, 0), (2, 1), 1),   # y expanded: 5 taps at stride 3, 2 x 2
-    ((3, 3), (2, 2), (1, 1), (0, 0), (3, 3), 2),   # expanded: 7 taps at stride 2, 4 x 4
+    ((3, 3), (2, 2), (1, 1), (0, 0), (3, 3), 1),   # expanded: 7 taps at stride 2, 4 x 4 (tap groups)
     ((4, 2), (2, 2), (1, 2), (0, 1), (1, 3), 1),   # x expanded to 4 taps: 2 x 2
     ((3, 3), (1, 1), (1, 1), (0, 0), (1, 1), 1),   # 3 x 3 taps without dilation
     ((5, 5), (2, 2), (2, 2), (1, 1), (1, 1), 1),   # 3 x 3 taps per phase
@@ -208,7 +209,8 @@ def test_route_rule(lib, k, s, p, op, d, route):
 def test_route_rule_2d_dilation(lib, k, s, p, op, d, route):
     # 2-D: per dimension reduction by gcd(s, d) and expansion of the rest of
     # the dilation; the compiled 2-D tap counts are 1 or 2 per dimension, or
-    # 3 x 3; any number of phases (column tiles take subsets of them)
+    # 3 x 3 (fp32 without a reduction: any count, in tap groups); any number
+    # of phases (column tiles take subsets of them)
     assert C.ctconv_query_route(2, 16, 16, (20, 22), k, s, p, op, d, 0) == route
 
 

@@ -137,6 +137,12 @@ FULL_CASES = [
     ("s3_2d_f32_k3", "f32", 1, 40, 64, (21, 10), (3, 3), (3, 3), (0, 1), (2, 0), (1, 1), False),
     ("s4_2d_f16", "f16", 2, 36, 24, (9, 11), (4, 4), (4, 4), (0, 0), (0, 0), (1, 1), True),
     ("s4x3_2d_f32", "f32", 1, 24, 96, (7, 15), (8, 6), (4, 3), (2, 1), (0, 1), (1, 1), True),
+    # fp32 with more taps per phase than an instance: tap groups
+    ("taps8_1d_f32", "f32", 2, 40, 24, (300,), (16,), (2,), (7,), (0,), (1,), True),
+    ("taps6_1d_f32", "f32", 1, 33, 17, (211,), (12,), (2,), (3,), (1,), (1,), True),
+    ("taps4x4_2d_f32", "f32", 1, 24, 32, (19, 23), (7, 7), (2, 2), (3, 3), (1, 0), (1, 1), True),
+    ("taps_dil3_2d_f32", "f32", 1, 20, 16, (17, 13), (3, 3), (2, 2), (1, 1), (0, 0), (3, 3), False),
+    ("taps12_1d_f32_s1", "f32", 2, 16, 40, (90,), (12,), (1,), (5,), (0,), (1,), True),
     # odd input rows (2-byte-offset row pieces): odd length with ragged
     # channels, and a 2-D plane of odd size (odd channels 2 bytes off)
     ("odd_len_bf16", "bf16", 2, 40, 24, (301,), (8,), (4,), (2,), (0,), (1,), True),
@@ -291,6 +297,9 @@ ACT_CASES = [
     ("act_f32_2d", "f32", 2, 24, 20, (13, 11), (4, 4), (2, 2), (1, 1), (0, 0), (1, 1), True),
     ("act_f16_gather_dil", "f16", 1, 40, 12, (37,), (5,), (3,), (2,), (1,), (2,), True),
     ("act_dil2_2d_f32", "f32", 1, 24, 20, (13, 11), (3, 3), (2, 2), (1, 1), (1, 1), (2, 2), True),
+    # tap groups: the activation after the last group's sum
+    ("act_f32_taps8", "f32", 1, 24, 16, (100,), (16,), (2,), (7,), (0,), (1,), True),
+    ("act_f32_2d_taps4x3", "f32", 1, 20, 24, (11, 9), (7, 5), (2, 2), (2, 1), (1, 0), (1, 1), True),
 ]
 
 

@@ -179,6 +179,12 @@ struct PolyArgs {
     // dilation) and writes its output o' as output o' - os of that problem
     // when it lies inside, i.e. below Ho - os (Wo - os)
     int oys, oxs;
+    // Tap groups (fp32 shapes with more taps per phase than a compiled
+    // kernel instance): launch g runs tap slots r0 .. r0 + MY/MX - 1 of every
+    // phase on the input window shifted back by r0, and launches after the
+    // first add their sums to y (accum = 1; the bias comes with the first,
+    // the activation with the last, after its sum)
+    int r0y, r0x, accum, ngy, ngx, gmy, gmx;  // gmy, gmx: tap slots per group
     // Packed-weight geometry (the real stride and taps the weight was packed
     // with): the kernel's tap e = s' r + j per dimension is real tap t = e / d',
     // stored as phase t mod ps, tap t / ps; other taps and t >= k read as zero.

@@ -145,8 +145,9 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     // for every phase unless the phase rows are output-aligned under
     // padding): the window starts m - 1 rows before the tile's smallest
     // delta
-    const int wy0 = ay0 + a.dminy - (MY - 1);
-    const int wx0 = ax0 + a.dminx - (MX - 1) - a.xofs;
+    // (a tap group starting at slot r0 reads r0 rows and columns further back)
+    const int wy0 = ay0 + a.dminy - (MY - 1) - a.r0y;
+    const int wx0 = ax0 + a.dminx - (MX - 1) - a.r0x - a.xofs;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
@@ -309,7 +310,7 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                 // real stride s.  Missing taps read as zero (an offset past the
                 // packed weight, which is below 2^31 bytes: the range check of
                 // the load returns zeros).
-                const int ey = a.sy * (r / MX) + jy, ex = a.sx * (r % MX) + jx;
+                const int ey = a.sy * (r / MX + a.r0y) + jy, ex = a.sx * (r % MX + a.r0x) + jx;
                 const int ty = (int)fdiv((uint32_t)ey, a.fd_dey), tx = (int)fdiv((uint32_t)ex, a.fd_dex);
                 if (ty * a.dey == ey && tx * a.dex == ex && ty < a.kH && tx < a.kW) {
                     const int qy = (int)fdiv((uint32_t)ty, a.fd_psy);
@@ -950,7 +951,8 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
             }
         }
     };
-    if (a.act == CTCONV_ACT_ELU)
+    // (a launch that adds to y applies the activation after its sum, below)
+    if (a.act == CTCONV_ACT_ELU && !a.accum)
         stage_all(std::true_type{});
     else
         stage_all(std::false_type{});
@@ -997,6 +999,26 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                 s0v[u] = s0;
                 gb[u] = ((n * a.C_out + co) * a.HoR + oy) * a.WoR + ox0;
                 v[u] = *reinterpret_cast<const u32x4*>(smem + sof[u] + s0);
+            }
+            if constexpr (sizeof(S) == 4) {
+                if (a.accum) {
+                    // a later tap group: y += the staged sums (then the
+                    // activation, in the last group)
+                    const bool elu = a.act == CTCONV_ACT_ELU;
+                    auto fin = [&](float o, float t) __attribute__((always_inline)) {
+                        const float r = o + t;
+                        return elu ? elu_act<TR>(r) : r;
+                    };
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        if (!ok[u]) continue;
+                        const int s0 = s0v[u];
+                        const int qb = s0 < lo ? lo : s0, qe = s0 + VEC < lim ? s0 + VEC : lim;
+                        for (int q = qb; q < qe; ++q)
+                            yg[gb[u] + q] = fin(yg[gb[u] + q], smem[sof[u] + q]);
+                    }
+                    continue;
+                }
             }
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -1458,13 +1480,34 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allow_spl
     // or column (a tile dimension the phase rows fit exactly), class mode
     // keeps output-aligned phase rows instead: the phases then read inputs
     // from different offsets, each 16-column block its own.
+    // Tap groups: fp32 shapes (without a dilation reduction) with more taps
+    // per phase than the compiled instances (1-D: 4; 2-D: 2 x 2, or 3 x 3)
+    // run as a sequence of launches of at most that many tap slots each
+    int gmy = 0, gmx = 0;
+    const int64_t mH0 = q.mH, mW0 = q.mW;
+    if (!reduced && p.dtype == CTCONV_F32) {
+        if (q.ndim == 1 && q.mW > 4) {
+            gmy = 1;
+            gmx = 4;
+        } else if (q.ndim == 2 && (q.mH > 2 || q.mW > 2) && !(q.mH == 3 && q.mW == 3)) {
+            gmy = q.mH > 2 ? 2 : (int)q.mH;
+            gmx = q.mW > 2 ? 2 : (int)q.mW;
+        }
+    }
+    const bool grouped = gmx > 0;
+    if (grouped) {
+        q.mH = gmy;
+        q.mW = gmx;
+        q.T = q.mH * q.mW;
+        allow_split = false;
+    }
     Problem qs = q;
     qs.Ho += qs.pH;
     qs.Wo += qs.pW;
     qs.pH = qs.pW = 0;
     if (qs.Ho == 0 || qs.Wo == 0) return false;
     bool cmode = false;
-    if (q.pH % q.sH != 0 || q.pW % q.sW != 0) {
+    if (!grouped && (q.pH % q.sH != 0 || q.pW % q.sW != 0)) {
         PolyArgs ac{};
         Inst ic{};
         int spc = 1;
@@ -1522,6 +1565,16 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allow_spl
     a->kW = (int)p.kW;
     a->fd_psy = make_fastdiv((uint32_t)p.sH);
     a->fd_psx = make_fastdiv((uint32_t)p.sW);
+    a->r0y = a->r0x = a->accum = 0;
+    a->ngy = a->ngx = 1;
+    a->gmy = (int)q.mH;
+    a->gmx = (int)q.mW;
+    if (grouped) {
+        // every group adds into y through the flattened stores
+        if (a->phase_subset || a->partial || *splits != 1) return false;
+        a->ngy = (int)((mH0 + gmy - 1) / gmy);
+        a->ngx = (int)((mW0 + gmx - 1) / gmx);
+    }
     return true;
 }
 
@@ -1597,6 +1650,29 @@ hipError_t launch_polyphase(const Problem& p, const void* x, const void* pw, con
         if (e != hipSuccess) return e;
     }
     const int64_t tiles = a.n_tiles;
+    if (a.ngy * a.ngx > 1) {
+        // tap groups, in order on the stream: the first writes y with the
+        // bias, the others add to it, the last applies the activation
+        const int G = a.ngy * a.ngx;
+        const int es = p.dtype == CTCONV_F32 ? 4 : 2, np = 8 / es;
+        for (int gy = 0; gy < a.ngy; ++gy)
+            for (int gx = 0; gx < a.ngx; ++gx) {
+                const int g = gy * a.ngx + gx;
+                PolyArgs ag = a;
+                ag.r0y = gy * a.gmy;
+                ag.r0x = gx * a.gmx;
+                // x loads stay aligned: the window start moves back by r0x
+                const int w0 = a.dminx - (a.gmx - 1) - ag.r0x;
+                ag.xofs = (a.W * es) % 4 == 0 ? ((w0 % np) + np) % np : 0;
+                ag.accum = g > 0 ? 1 : 0;
+                ag.bias = g == 0 ? bias : nullptr;
+                ag.act = g == G - 1 ? act : CTCONV_ACT_NONE;
+                hipLaunchKernelGGL(in.fn, dim3((unsigned)tiles, 1u), dim3(in.threads), 0, s, ag);
+                const hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+            }
+        return hipSuccess;
+    }
     hipLaunchKernelGGL(in.fn, dim3((unsigned)tiles, (unsigned)splits), dim3(in.threads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !a.partial) return e;
