@@ -30,6 +30,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "ConvTranspose TFLOP/s (2*N*Cin*Cout*K*Lin) and % of MFMA/HBM roofline, 1 GPU"
+# ctconv_route codes of the dense layers' kernels (include/ctconv.h)
+ROUTES = {"auto": 0, "gather": 2, "tiled": 3, "stream": 4}
 PEAK_MFMA = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # dense TFLOP/s
 PEAK_HBM = 8000.0  # GB/s
 # fp32 vector arithmetic (the gather kernel's FMAs, every dtype): 256 CUs x
@@ -55,6 +57,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="vocoder_stack")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--route", default="auto", choices=sorted(ROUTES),
+                    help="kernel for the dense layers (default: the library's choice); "
+                         "'gather' measures the gather fallback on the same shapes")
     ap.add_argument("--no-clock-probe", action="store_true",
                     help="skip the sustained-clock probe (about 2 ms of GPU time after the timing)")
     ap.add_argument("--cold-reps", type=int, default=20,
@@ -328,9 +333,12 @@ def main():
     fuse = wl.elu_between and not args.separate_elu
     # dense layers go through ctconv_forward_ws: shapes with few output tiles
     # split their reduction into a workspace (deterministic); the others need none
-    convs = [(C.DepthwiseConv if L.groups > 1 else C.ConvWS)(
+    # (a forced kernel goes through ctconv_forward_act, without a workspace)
+    forced = ROUTES[args.route]
+    convs = [(C.DepthwiseConv if L.groups > 1 else C.ConvWS if forced == 0 else C.Conv)(
                  wl.N, L.C_in, L.C_out, sp, L.kernel, L.stride, L.padding, L.output_padding,
-                 L.dilation, dcode, act=C.ACT_ELU if (fuse and li + 1 < len(geo)) else C.ACT_NONE)
+                 L.dilation, dcode, act=C.ACT_ELU if (fuse and li + 1 < len(geo)) else C.ACT_NONE,
+                 **({} if (L.groups > 1 or forced == 0) else {"route": forced}))
              for li, (L, sp, osp, _, _) in enumerate(geo)]
     wspaces = [torch.empty(max(getattr(cv, "ws_bytes", 0), 16), dtype=torch.uint8, device="cuda")
                if getattr(cv, "ws_bytes", 0) > 0 else None for cv in convs]
@@ -444,6 +452,8 @@ def main():
             route = 10 + C.ctconv_depthwise_query_kernel(
                 wl.N, L.C_in, L.C_out, sp, L.kernel, L.stride, L.padding, L.output_padding,
                 L.dilation, dcode)
+        elif forced != 0:
+            route = 2 if forced == 2 else 1
         else:
             route = C.ctconv_query_route(wl.N, L.C_in, L.C_out, sp, L.kernel, L.stride,
                                          L.padding, L.output_padding, L.dilation, dcode)
@@ -519,6 +529,7 @@ def main():
         "dtype": wl.dtype,
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {"workload": wl.name, "description": wl.note, "N": wl.N,
+                   "route": args.route,
                    "in_spatial": list(wl.in_spatial), "parallelism": "none (1 GPU)",
                    "elu": ("fused into the producing layer" if fuse else
                            "separate pass" if wl.elu_between else "none"),
