@@ -49,6 +49,10 @@
 // the caller gives a workspace): each split writes its fp32 partial sums to y
 // or to a workspace slab with plain stores, and a second kernel adds them in
 // a fixed order, so results are the same bits on every run.
+// More phases than a column tile holds: each column tile takes a subset of
+// whole phases.  More taps per phase than an instance (fp32): launches over
+// groups of tap slots, each on the input window shifted back by its first
+// slot, the later ones adding to y in launch order.
 
 #include <type_traits>
 
@@ -1471,15 +1475,6 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allow_spl
     if (!reduce_dilation(p, &rd)) return false;
     Problem& q = rd.q;
     const bool reduced = rd.g[0] > 1 || rd.g[1] > 1;
-    // Padding as an output shift: output o of the padded problem is output
-    // o + p of the same transposed convolution without padding, so the kernel
-    // runs that one (outputs o' in [0, L_out + p)) and writes o' - p when it
-    // lies in [0, L_out).  Without padding output phase b reads inputs
-    // q - r for every phase alike (no phase-dependent input offset).
-    // When that adds a phase row or column that costs a whole extra tile row
-    // or column (a tile dimension the phase rows fit exactly), class mode
-    // keeps output-aligned phase rows instead: the phases then read inputs
-    // from different offsets, each 16-column block its own.
     // Tap groups: fp32 shapes (without a dilation reduction) with more taps
     // per phase than the compiled instances (1-D: 4; 2-D: 2 x 2, or 3 x 3)
     // run as a sequence of launches of at most that many tap slots each
@@ -1501,6 +1496,15 @@ bool plan(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allow_spl
         q.T = q.mH * q.mW;
         allow_split = false;
     }
+    // Padding as an output shift: output o of the padded problem is output
+    // o + p of the same transposed convolution without padding, so the kernel
+    // runs that one (outputs o' in [0, L_out + p)) and writes o' - p when it
+    // lies in [0, L_out).  Without padding output phase b reads inputs
+    // q - r for every phase alike (no phase-dependent input offset).
+    // When that adds a phase row or column that costs a whole extra tile row
+    // or column (a tile dimension the phase rows fit exactly), class mode
+    // keeps output-aligned phase rows instead: the phases then read inputs
+    // from different offsets, each 16-column block its own.
     Problem qs = q;
     qs.Ho += qs.pH;
     qs.Wo += qs.pW;
