@@ -20,18 +20,23 @@
  *    as one polyphase conv + depth to space", Summary formula).  The same
  *    holds for any k with m = ceil(k / s) taps per phase, the taps past k
  *    being zero in the packed weight, and output_padding only lengthens the
- *    output, so this route takes every shape with dilation 1.  It runs as an
- *    implicit GEMM on the MFMA matrix cores with the interleave, slice and
- *    bias fused into its epilogue, for m <= 4 (1-D), m <= 2 or m = 3 per
- *    dimension (2-D: 1x1, 1x2, 2x1, 2x2 or 3x3 taps) and input rows of at
- *    least 8 bytes (W >= 4 for bf16/fp16, W >= 2 for fp32).  In 2-D a
- *    dilation d that divides the stride is taken too: only outputs o with
- *    o + p divisible by d receive taps, and they form the transposed
- *    convolution with stride s / d and dilation 1 over (o - o0) / d; when
- *    that reduced problem has 3x3 taps (e.g. k = 3, s = d = 2) it runs on
- *    this route after a bias fill of the other outputs.
- *  - gather: every other shape (other dilations, more taps, shorter rows),
- *    one output at a time from the tap condition.
+ *    output.  It runs as an implicit GEMM on the MFMA matrix cores with the
+ *    interleave, slice, bias and activation fused into its epilogue.  A
+ *    dilation d is reduced by g = gcd(s, d) per dimension (only outputs
+ *    o0 + g*u receive taps: a transposed convolution with stride s / g,
+ *    after a bias fill of the other outputs) and the rest d / g expanded
+ *    into zero taps.  Compiled kernel instances take at most 4 taps per
+ *    phase in 1-D and 1 or 2 per dimension, or 3 x 3, in 2-D; fp32 shapes
+ *    without a dilation reduction take any number, as a sequence of
+ *    launches over groups of taps that add into y in order.  Column tiles
+ *    hold a subset of the phases when there are more than a tile holds
+ *    (e.g. 2-D stride 3).  Input rows must be at least 8 bytes (W >= 4 for
+ *    bf16/fp16, W >= 2 for fp32).
+ *  - gather: every other shape (16-bit shapes with more taps per phase than
+ *    an instance, reduced dilations with too many taps, shorter rows): a
+ *    gather-form kernel that stages x and the taps' weights in LDS and
+ *    reduces over C_in across lanes, or one output and 8 channels per lane
+ *    for small problems and shapes past its staging limits.
  *
  * Layouts.  x [N, C_in, L] or [N, C_in, H, W]; y [N, C_out, L_out] or
  * [N, C_out, H_out, W_out]; bias [C_out]; all dense row-major (contiguous).
@@ -39,8 +44,9 @@
  * and rounded once (round to nearest even) to the output type.
  *
  * Ownership.  The caller allocates and owns every buffer.  The library never
- * allocates, frees, retains or aliases caller memory, and holds no global
- * mutable state; all functions are thread-safe.
+ * allocates, frees, retains or aliases caller memory.  Its only global
+ * mutable state is the fixed per-device scratch of ctconv_forward_noalloc
+ * (see there); every other function is thread-safe.
  *
  * Streams.  Device work is enqueued on `stream` (a hipStream_t; NULL is the
  * default stream) and the call returns without synchronising.  Errors found
