@@ -225,6 +225,21 @@ def test_route_short_rows(lib, sp, dt, route):
     assert C.ctconv_query_route(2, 16, 16, sp, k, s, p, 0, 1, dt) == route
 
 
+def test_planner_cases_reach_polyphase(lib):
+    """The seeded random set aimed at phase subsets and tap groups keeps
+    exercising them: most of its shapes are planned onto the polyphase route
+    (the rest, 2-D tap groups over 16 phases and rows under 8 bytes, go to
+    the gather kernel)."""
+    from random_cases import PLANNER_CASES
+
+    dts = {"f32": 0, "bf16": 1, "f16": 2}
+    hits = {"subset": 0, "groups": 0}
+    for kind, dt, N, C_in, C_out, sp, k, s, p, op, d, _, _ in PLANNER_CASES:
+        if C.ctconv_query_route(N, C_in, C_out, sp, k, s, p, op, d, dts[dt]) == 1:
+            hits[kind] += 1
+    assert hits["subset"] >= 12 and hits["groups"] >= 12, hits
+
+
 def test_stream_sizes(lib):
     # chunk of L frames: L*s outputs, k - s tail values, conv workspace
     # (the chunk's conv output is fp32 in every dtype)

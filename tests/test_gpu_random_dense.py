@@ -76,3 +76,32 @@ def test_dense_random_shapes(cc, case):
         torch.cuda.synchronize()
         check_parity(to_host(y), ref, mag, dt, terms_per_output(C_in, k, s, d),
                      f"{case} route={route}")
+
+
+# ---------------------------------------------------------------------------
+# the polyphase route's 2-D phase subsets and fp32 tap groups on random shapes
+
+from random_cases import PLANNER_CASES  # noqa: E402
+
+
+@pytest.mark.parametrize("case", PLANNER_CASES,
+                         ids=[f"{c[0]}{i}" for i, c in enumerate(PLANNER_CASES)])
+def test_planner_paths_random_shapes(cc, case):
+    import torch
+
+    from oracle import elu as oelu
+
+    kind, dt, N, C_in, C_out, sp, k, s, p, op, d, has_b, act = case
+    x64 = I.normal(800 + C_in, (N, C_in) + sp, 1.0, dt)
+    w64 = I.normal(900 + C_out, (C_in, C_out) + k, (C_in * float(np.prod(k))) ** -0.5, dt)
+    b64 = I.uniform(1000 + C_out, (C_out,), -0.1, 0.1, dt) if has_b else None
+    ref, mag = ref_and_mag(x64, w64, b64, s, p, op, d)
+    if act:
+        ref = oelu(ref)  # 1-Lipschitz: the element bound on the sum carries over
+    pw = cc.prepack(to_dev(w64, dt), s)
+    for route in (0, 2):
+        y = cc.forward(to_dev(x64, dt), pw, None if b64 is None else to_dev(b64, dt), C_out, k,
+                       s, p, op, d, route=route, act=cc.ACT_ELU if act else cc.ACT_NONE)
+        torch.cuda.synchronize()
+        check_parity(to_host(y), ref, mag, dt, terms_per_output(C_in, k, s, d),
+                     f"{case} route={route}", abs_slack=1e-6 if act else 0.0)
