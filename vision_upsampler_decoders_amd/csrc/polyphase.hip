@@ -211,6 +211,26 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     // unconditional.
     int xlds[C::XITEMS];
     bool inside = true;  // the lane's items need no realignment or masks
+    // Bank spreading of the transposed stores (16-bit: four positions per
+    // item).  Consecutive lanes own items four position rows apart, i.e. 4 x
+    // 80 bytes, which is 64 bytes modulo the 256 bytes that one pass of the
+    // LDS covers: the same position of 16 consecutive lanes would fall into
+    // four bank groups only.  So lane l first rotates its item's positions by
+    // rho(l) and store j writes position (j + rho) mod 4: within every 8-lane
+    // group (bits 1-2 of l) and every 16-lane group (bits 2-3 of l) with the
+    // other bits fixed, rho takes all four values, which puts the stores of
+    // one pass into distinct 16-byte bank groups for a 128-byte or a 256-byte
+    // pass.  rho = bit 2 of l as its high bit, bit 1 xor bit 3 of l as its
+    // low bit; the rotation is two byte permutes per channel.
+    constexpr bool ROT = C::ES == 2;
+    const int rho = ROT ? ((((lane >> 1) ^ (lane >> 3)) & 1) | ((lane >> 1) & 2)) : 0;
+    // v_perm selectors: the dword of positions (r, r + 1) mod 4 of a channel
+    // held as positions 0-3 in two dwords (bytes 2 p, 2 p + 1 of the pair)
+    auto rot_sel = [](int r) -> uint32_t {
+        const uint32_t b0 = 2u * (uint32_t)(r & 3), b1 = 2u * (uint32_t)((r + 1) & 3);
+        return b0 | (b0 + 1u) << 8 | b1 << 16 | (b1 + 1u) << 24;
+    };
+    const uint32_t rsel_lo = rot_sel(rho), rsel_hi = rot_sel(rho + 2);
 #pragma unroll
     for (int it = 0; it < C::XITEMS; ++it) {
         const int qw = lane + 64 * it;
@@ -285,12 +305,20 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     // phases: the load is made anyway so that no load sits under a branch;
     // such rows feed only columns that are never stored) and LDS slot (row
     // padding for lanes without one).
+    // The 64 items of one load instruction are 16 rows of NG = 4 pieces.
+    // Lanes take them in the order that puts rows 0, 4, 8, 12 (then 1, 5, 9,
+    // 13, ...) into one 16-lane pass of the LDS store: those rows start 80 r
+    // bytes in, i.e. 0, 64, 128 and 192 modulo 256, so their 64-byte runs
+    // fill distinct bank groups (four consecutive rows would span 320
+    // bytes and meet twice).  The instruction reads the same rows of global
+    // memory as in lane order.
     uint32_t boff[C::BITEMS];
     int blds[C::BITEMS];
     constexpr int bper = (C::BMAX + C::NW - 1) / C::NW;
+    const int bl = (lane & 3) | ((lane >> 4) << 2) | (((lane >> 2) & 3) << 4);
 #pragma unroll
     for (int it = 0; it < C::BITEMS; ++it) {
-        const int qw = lane + 64 * it;
+        const int qw = bl + 64 * it;
         const int q = wave * bper + qw;
         boff[it] = 0;
         blds[it] = (lane % C::BROWS) * RSA + KC;  // row padding: no item
@@ -412,6 +440,14 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                 }
             }
         };
+        // (16-bit) position j of every channel of the item <- position
+        // (j + rho) mod 4, so that the transpose's row j is that position
+        auto rotate = [&](u32x2 (&in)[VEC]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+                in[e] = u32x2{__builtin_amdgcn_perm(in[e][1], in[e][0], rsel_lo),
+                              __builtin_amdgcn_perm(in[e][1], in[e][0], rsel_hi)};
+        };
         if (decltype(inside)::value || wave_inside) {
             // no lane of the wave touches a row edge: transpose and store only
 #pragma unroll
@@ -419,10 +455,11 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                 u32x2 in[VEC];
                 u32x4 tr[NP];
                 pieces(it, in);
+                if constexpr (ROT) rotate(in);
                 transpose_block(in, tr);
 #pragma unroll
                 for (int p = 0; p < NP; ++p)
-                    *reinterpret_cast<u32x4*>(xs + xlds[it] + p * RSA) = tr[p];
+                    *reinterpret_cast<u32x4*>(xs + xlds[it] + ((p + rho) & (NP - 1)) * RSA) = tr[p];
             }
         } else {
             // every lane realigns (shift 0 away from row edges) and zeroes
@@ -440,11 +477,13 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
                     v = sh >= 0 ? (v >> sh) : (v << -sh);
                     in[e] = __builtin_bit_cast(u32x2, v);
                 }
+                if constexpr (ROT) rotate(in);
                 transpose_block(in, tr);
 #pragma unroll
-                for (int p = 0; p < NP; ++p)
-                    *reinterpret_cast<u32x4*>(xs + xlds[it] + p * RSA) =
-                        (m & (1u << p)) ? tr[p] : z;
+                for (int p = 0; p < NP; ++p) {
+                    const int pr = (p + rho) & (NP - 1);  // the position row tr[p] holds
+                    *reinterpret_cast<u32x4*>(xs + xlds[it] + pr * RSA) = (m & (1u << pr)) ? tr[p] : z;
+                }
             }
         }
         // B rows past C_out or past the phases feed only columns that are
