@@ -213,15 +213,16 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     bool inside = true;  // the lane's items need no realignment or masks
     // Bank spreading of the transposed stores (16-bit: four positions per
     // item).  Consecutive lanes own items four position rows apart, i.e. 4 x
-    // 80 bytes, which is 64 bytes modulo the 256 bytes that one pass of the
-    // LDS covers: the same position of 16 consecutive lanes would fall into
-    // four bank groups only.  So lane l first rotates its item's positions by
-    // rho(l) and store j writes position (j + rho) mod 4: within every 8-lane
-    // group (bits 1-2 of l) and every 16-lane group (bits 2-3 of l) with the
-    // other bits fixed, rho takes all four values, which puts the stores of
-    // one pass into distinct 16-byte bank groups for a 128-byte or a 256-byte
-    // pass.  rho = bit 2 of l as its high bit, bit 1 xor bit 3 of l as its
-    // low bit; the rotation is two byte permutes per channel.
+    // 80 bytes, which is 64 bytes modulo the 256 bytes of the 64 banks: in
+    // lane order the same position of 16 consecutive lanes falls into four
+    // bank groups only, and a probe of that store pattern alone measured it
+    // 4-way conflicted on gfx950.  So lane l first rotates its item's
+    // positions by rho(l) and store j writes position (j + rho) mod 4:
+    // within every 8-lane group (bits 1-2 of l) and every 16-lane group
+    // (bits 2-3 of l) with the other bits fixed, rho takes all four values
+    // (bit 2 of l as its high bit, bit 1 xor bit 3 of l as its low bit); the
+    // same probe measured the rotated pattern free of conflicts.  The
+    // rotation is two byte permutes per channel.
     constexpr bool ROT = C::ES == 2;
     const int rho = ROT ? ((((lane >> 1) ^ (lane >> 3)) & 1) | ((lane >> 1) & 2)) : 0;
     // v_perm selectors: the dword of positions (r, r + 1) mod 4 of a channel
@@ -307,10 +308,11 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     // padding for lanes without one).
     // The 64 items of one load instruction are 16 rows of NG = 4 pieces.
     // Lanes take them in the order that puts rows 0, 4, 8, 12 (then 1, 5, 9,
-    // 13, ...) into one 16-lane pass of the LDS store: those rows start 80 r
-    // bytes in, i.e. 0, 64, 128 and 192 modulo 256, so their 64-byte runs
-    // fill distinct bank groups (four consecutive rows would span 320
-    // bytes and meet twice).  The instruction reads the same rows of global
+    // 13, ...) into 16 consecutive lanes: those rows start 80 r bytes in,
+    // i.e. 0, 64, 128 and 192 modulo 256, so their 64-byte runs fill
+    // distinct bank groups (four consecutive rows span 320 bytes and meet
+    // twice: 2-way conflicted in lane order, conflict-free in this order, as
+    // probed on gfx950).  The instruction reads the same rows of global
     // memory as in lane order.
     uint32_t boff[C::BITEMS];
     int blds[C::BITEMS];
