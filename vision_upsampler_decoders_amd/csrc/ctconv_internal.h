@@ -159,6 +159,9 @@ struct PolyArgs {
     float* ws;             // the slabs (partial = 1)
     int64_t ws_slab;       // elements per slab (the size of y)
     int xcd_remap;         // 1: gridDim.x is a multiple of 8, remap for L2 locality
+    int colmajor;          // tile order: 1 all row tiles of a column tile, then the
+                           // next column tile; 0 all column tiles of a row tile first
+    FastDiv fd_rows;       // n_row_tiles
     uint32_t pw_bytes;     // size of the packed weight (below 2^32)
     int act;               // ctconv_activation of the epilogue
     int outf32;            // 1: y is fp32, written straight from the accumulators (1-D
