@@ -129,7 +129,7 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
 
     // ---- tile coordinates -------------------------------------------------
     // linear tile = row_tile * n_col_tiles + col (row-major order) or
-    // col * n_row_tiles + row_tile (column-major order, for shapes whose
+    // col * n_row_tiles + row_tile (column-major order, for fp32 shapes whose
     // packed weight outweighs their input), row_tile = (n * tiles_y + ty) *
     // tiles_x + tx; with the XCD remap the gridDim.x / 8 workgroups of one
     // XCD (dispatched round robin) take a contiguous run of tiles, so that
@@ -137,16 +137,18 @@ __global__ __launch_bounds__(64 * WM * WN, (RB * CB >= 64 ? 1 : 2)) void poly_ke
     // rows (column-major) meet in one L2
     uint32_t bid = blockIdx.x;
     if (a.xcd_remap) bid = (bid % 8u) * (gridDim.x / 8u) + bid / 8u;
-    uint32_t row_tile;
-    int col_tile;
-    if (a.colmajor) {
-        const uint32_t cq = fdiv(bid, a.fd_rows);
-        row_tile = bid - cq * (uint32_t)a.n_row_tiles;
-        col_tile = (int)cq;
-    } else {
-        row_tile = fdiv(bid, a.fd_cols);
-        col_tile = (int)(bid - row_tile * (uint32_t)a.n_col_tiles);
+    // (fp32 instances only: in the 16-bit ones the remap's extra uniform
+    // values tip the scalar registers into spills that cost the vocoder
+    // layers 5 % and the 2-D upsampler 8 %)
+    if constexpr (C::ES == 4) {
+        if (a.colmajor) {
+            // the column-major position of bid as its row-major tile index
+            const uint32_t cq = fdiv(bid, a.fd_rows);
+            bid = (bid - cq * (uint32_t)a.n_row_tiles) * (uint32_t)a.n_col_tiles + cq;
+        }
     }
+    const uint32_t row_tile = fdiv(bid, a.fd_cols);
+    const int col_tile = (int)(bid - row_tile * (uint32_t)a.n_col_tiles);
     const uint32_t rt2 = fdiv(row_tile, a.fd_tx);
     const int tx_t = (int)(row_tile - rt2 * (uint32_t)a.tiles_x);
     const uint32_t nq = fdiv(rt2, a.fd_ty);
@@ -1439,11 +1441,11 @@ bool plan_core(const Problem& p, PolyArgs* a, Inst* inst, int* splits, bool allo
         // slowest along it: row-major shares the input rows and needs every
         // column tile's weights, column-major the reverse.  Take the order
         // that keeps the larger operand shared (the iSTFT basis, 67 MB
-        // against 45 MB of frames, halves the kernel's fetched bytes that way).
-        const int64_t es = p.dtype == CTCONV_F32 ? 4 : 2;
-        const int64_t w_bytes = P * p.C_out * p.T * p.C_in_pad * es;
-        const int64_t x_bytes = p.N * p.C_in_pad * p.H * p.W * es;
-        a->colmajor = w_bytes > x_bytes ? 1 : 0;
+        // against 45 MB of frames, halves the kernel's fetched bytes that
+        // way).  fp32 only: the 16-bit instances are compiled row-major.
+        const int64_t w_bytes = P * p.C_out * p.T * p.C_in_pad * 4;
+        const int64_t x_bytes = p.N * p.C_in_pad * p.H * p.W * 4;
+        a->colmajor = p.dtype == CTCONV_F32 && w_bytes > x_bytes ? 1 : 0;
     }
     a->n_tiles = (uint32_t)tiles;
     a->fd_cols = make_fastdiv((uint32_t)n_col_tiles);
